@@ -1,0 +1,64 @@
+"""Test-side glue: oracle caches from a Workload, and comparison metrics."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from paged_kv_cache_267_amd.workloads import NP_STORAGE, POISON_BYTE, Workload
+
+
+def cache_elems(wl: Workload) -> int:
+    return wl.num_blocks * wl.num_kv_heads * wl.head_dim * wl.block_size
+
+
+def poison_cache(wl: Workload) -> np.ndarray:
+    dt = NP_STORAGE[wl.kv_dtype]
+    n = cache_elems(wl)
+    return np.full(n * np.dtype(dt).itemsize, POISON_BYTE, dtype=np.uint8).view(dt)
+
+
+def oracle_caches(wl: Workload, *, with_new: bool = True):
+    """Key/value caches as the oracle fills them: history, then the new tokens."""
+    kc, vc = poison_cache(wl), poison_cache(wl)
+    kw = dict(num_kv_heads=wl.num_kv_heads, head_dim=wl.head_dim, block_size=wl.block_size,
+              num_blocks=wl.num_blocks, kv_dtype=wl.kv_dtype)
+    oracle.reshape_and_cache(wl.hist_key, wl.hist_value, kc, vc, wl.hist_slots, **kw)
+    if with_new:
+        oracle.reshape_and_cache(wl.new_key, wl.new_value, kc, vc, wl.new_slots, **kw)
+    return kc, vc
+
+
+def oracle_decode(wl: Workload, kc, vc, rows=None, **over) -> np.ndarray:
+    kw = dict(block_size=wl.block_size, scale=wl.scale, num_kv_heads=wl.num_kv_heads,
+              q_dtype=wl.q_dtype, kv_dtype=wl.kv_dtype, sliding_window=wl.sliding_window,
+              k_scale=wl.k_scale, v_scale=wl.v_scale, rows=rows)
+    kw.update(over)
+    return oracle.decode(wl.query, kc, vc, wl.block_tables, wl.seq_lens, **kw)
+
+
+def oracle_decode_split(wl: Workload, kc, vc, rows=None, **over):
+    kw = dict(block_size=wl.block_size, scale=wl.scale, num_kv_heads=wl.num_kv_heads,
+              q_dtype=wl.q_dtype, kv_dtype=wl.kv_dtype, sliding_window=wl.sliding_window,
+              k_scale=wl.k_scale, v_scale=wl.v_scale, rows=rows,
+              partition_size=wl.partition_size, max_partitions=wl.max_partitions)
+    kw.update(over)
+    return oracle.decode_split(wl.query, kc, vc, wl.block_tables, wl.seq_lens, **kw)
+
+
+def widen(raw: np.ndarray, dtype: str) -> np.ndarray:
+    """Element values as float64 via torch casts (independent of the oracle)."""
+    import torch
+    if dtype == "f32":
+        return raw.astype(np.float64)
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.bfloat16)
+        return t.to(torch.float64).numpy()
+    if dtype == "fp8_e4m3":
+        t = torch.from_numpy(np.ascontiguousarray(raw)).view(torch.float8_e4m3fn)
+        return t.to(torch.float64).numpy()
+    raise ValueError(dtype)
+
+
+def err_stats(got: np.ndarray, ref: np.ndarray):
+    d = np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))
+    return float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0

@@ -1,0 +1,86 @@
+"""Host-side checks of the seeded input generator (no GPU, no oracle arithmetic)."""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from paged_kv_cache_267_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_block_arithmetic_printed_on_the_pages():
+    facts = json.load(open(os.path.join(GOLDEN, "page_facts.json")))["facts"]
+    f64k, fceil, frange = facts
+    assert W.blocks_needed(f64k["num_tokens"], f64k["block_size"]) == f64k["blocks"]
+    for n, bs, expect in fceil["cases"]:
+        assert W.blocks_needed(n, bs) == expect
+    bs = frange["block_size"]
+    blk = {j // bs for j in range(frange["first"], frange["last"] + 1)}
+    assert len(blk) == 1
+    assert (frange["first"] - 1) // bs not in blk and (frange["last"] + 1) // bs not in blk
+
+
+def test_tables_slots_and_pool_are_consistent():
+    wl = W.random_case(5, seq_lens=[0, 1, 16, 17, 90], num_q_heads=4, num_kv_heads=2,
+                       head_dim=64, block_size=16)
+    bs = wl.block_size
+    used = []
+    for s, L in enumerate(wl.seq_lens):
+        nb = W.blocks_needed(int(L), bs)
+        assert (wl.block_tables[s, :nb] >= 0).all()
+        assert (wl.block_tables[s, nb:] == -1).all()
+        used += list(wl.block_tables[s, :nb])
+    assert len(set(used)) == len(used), "private blocks are never shared"
+    assert max(used) < wl.num_blocks
+    slots = np.concatenate([wl.hist_slots, wl.new_slots])
+    assert len(np.unique(slots)) == len(slots)
+    assert len(wl.new_slots) == int((wl.seq_lens > 0).sum())
+    assert len(slots) == int(wl.seq_lens.sum())
+
+
+def test_shared_prefix_tables():
+    wl = W.random_case(6, seq_lens=[40, 57, 33], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                       block_size=16, shared_prefix=32)
+    assert (wl.block_tables[:, :2] == wl.block_tables[0, :2]).all()
+    # the prefix tokens are written once
+    assert len(wl.hist_slots) + len(wl.new_slots) == 32 + int((wl.seq_lens - 32).sum())
+
+
+def test_poison_out_of_window_points_at_spare_block():
+    wl = W.random_case(8, seq_lens=[100, 20], num_q_heads=4, num_kv_heads=1, head_dim=64,
+                       block_size=16, sliding_window=40, poison_out_of_window=True)
+    spare = wl.block_tables[0, 0]
+    assert (wl.block_tables[0, :60 // 16] == spare).all()
+    dealt = set(np.concatenate([wl.hist_slots, wl.new_slots]) // 16)
+    assert spare not in dealt
+
+
+def test_generator_is_deterministic():
+    a = W.random_case(9, seq_lens=[5, 70], kv_dtype="fp8_e4m3")
+    b = W.random_case(9, seq_lens=[5, 70], kv_dtype="fp8_e4m3")
+    for f in ("query", "hist_key", "hist_value", "new_key", "block_tables", "seq_lens"):
+        assert np.array_equal(getattr(a, f), getattr(b, f))
+    assert a.k_scale == b.k_scale
+
+
+def test_config1_shape_and_bytes():
+    wl = W.config(1)
+    assert list(wl.seq_lens) == [1, 17, 33, 100]
+    assert wl.num_blocks == 64
+    assert wl.kv_bytes() == 151 * 4 * 64 * 2 * 4 == 309_248
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_named_configs_shapes(cfg):
+    wl = W.config(cfg)
+    if cfg == 2:
+        assert wl.num_seqs == 64 and wl.group == 4 and wl.block_size == 16
+        assert wl.seq_lens.min() >= 512 and wl.seq_lens.max() <= 4096
+    else:
+        assert wl.num_seqs == 128 and wl.group == 8
+        assert (wl.block_tables[:, :128] == wl.block_tables[0, :128]).all()
+        assert wl.unique_kv_bytes() < wl.kv_bytes()
