@@ -1,0 +1,192 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged decode-attention step on one MI355X.
+
+A step is one pass of the whole path over one batch: append each sequence's
+new token with pa_reshape_and_cache, attend with pa_decode_split (or
+pa_decode with --mode unsplit) and merge partitions with pa_reduce_lse.
+Inputs are seeded synthetic data already resident in HBM when timing starts.
+
+Prints ONE JSON line.  `value` is KV GB/s of the whole step (in-window K+V
+bytes read per step / wall time per step).  `roofline` is the decode kernel's
+algorithmic bytes per launch / its average launch time (HIP events on the
+launch stream) against 8 TB/s.  `cpu_baseline` times the CPU oracle on the
+host cores over the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode attention: KV GB/s (% of MI355X HBM peak) + µs/call"
+DEFAULT_CFG = 2
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    csrc = os.path.join(ROOT, "paged_kv_cache_267_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".h", ".hip", ".cpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def decode_algorithmic_bytes(wl, partition_size: int | None) -> int:
+    """Bytes the decode kernel must move per launch: in-window K+V, the query,
+    the block-table entries it reads, and its outputs (partials + LSEs when
+    split, the output rows otherwise)."""
+    import numpy as np
+    from paged_kv_cache_267_amd.workloads import ELEM_BYTES
+    eq = ELEM_BYTES[wl.q_dtype]
+    L = wl.seq_lens.astype(np.int64)
+    lo = np.maximum(0, L - wl.sliding_window) if wl.sliding_window > 0 else np.zeros_like(L)
+    bs = wl.block_size
+    blocks = np.where(L > lo, (L + bs - 1) // bs - lo // bs, 0)
+    table = int(blocks.sum()) * 4 * wl.num_kv_heads
+    q = wl.num_seqs * wl.num_q_heads * wl.head_dim * eq
+    if partition_size:
+        P = partition_size
+        parts = np.where(L > lo, (L + P - 1) // P - lo // P, 0)
+        out = int(parts.sum()) * wl.num_q_heads * (wl.head_dim + 1) * 4
+    else:
+        out = wl.num_seqs * wl.num_q_heads * wl.head_dim * eq
+    return wl.kv_bytes() + q + table + out
+
+
+def load_traffic(kernel_hash: str, workload: str, mode: str):
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    key = f"{workload}/{mode}"
+    r = rec.get(key)
+    if not r or r.get("kernel_hash") != kernel_hash:
+        return None
+    return r.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The oracle as it stands, on the host cores, over the whole workload;
+    repeated until at least budget_s seconds of work (at least once)."""
+    import oracle
+    from tests.helpers import oracle_caches, oracle_decode
+    kc, vc = oracle_caches(wl)
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle_decode(wl, kc, vc)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or runs >= 50:
+            break
+    return {"value": round(wl.kv_bytes() * runs / el / 1e9, 3), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"whole workload ({wl.num_seqs} seqs x {wl.num_q_heads} q heads), "
+                      f"{runs} run(s), {el:.1f} s, fp64, {round(el / runs * 1e3, 1)} ms/call"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=DEFAULT_CFG, help="workload 1..5")
+    ap.add_argument("--mode", choices=["split", "unsplit"], default="split")
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decode path has no multi-GPU leg "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from paged_kv_cache_267_amd import workloads as W
+    from paged_kv_cache_267_amd.harness import DeviceWorkload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = W.config(args.config)
+    split = args.mode == "split"
+    psize = args.partition_size or wl.partition_size
+    dw = DeviceWorkload(wl, partition_size=psize)
+    dw.fill_history()
+    torch.cuda.synchronize()
+    print(f"[bench] {wl.name}: {wl.description}; mode={args.mode} partition={psize}",
+          file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        dw.step(split=split)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        e = ev[k]
+        e[0].record(stream)
+        dw.append_new()
+        e[1].record(stream)
+        if split:
+            dw.decode_split()
+        else:
+            dw.decode_unsplit()
+        e[2].record(stream)
+        if split:
+            dw.reduce()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    T = time.perf_counter() - t0
+
+    ms_step = T / args.steps * 1e3
+    t_app = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
+    t_dec = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+    t_red = np.mean([e[2].elapsed_time(e[3]) for e in ev]) * 1e3 if split else 0.0
+    kv = wl.kv_bytes()
+    value = kv / (ms_step * 1e-3) / 1e9
+    alg = decode_algorithmic_bytes(wl, psize if split else None)
+    achieved = alg / (t_dec * 1e-6) / 1e9
+    khash = kernel_source_hash()
+    mode_key = f"{args.mode}{psize if split else ''}"
+    traffic = load_traffic(khash, wl.name, mode_key)
+
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"{wl.q_dtype} q / {wl.kv_dtype} kv, fp32 accumulate", "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description,
+                   "global_batch": wl.num_seqs, "seq_len_mean": float(wl.seq_lens.mean()),
+                   "seq_len_max": int(wl.seq_lens.max()), "mode": args.mode,
+                   "partition_size": psize if split else None, "parallelism": "single GPU"},
+        "step_breakdown_us": {"reshape_and_cache": round(t_app, 2), "decode": round(t_dec, 2),
+                              "reduce_lse": round(t_red, 2),
+                              "wall_per_step": round(ms_step * 1e3, 2)},
+        "kv_bytes_per_step": kv,
+        "pct_of_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "decode_valu_kernel",
+                     "algorithmic_bytes_per_launch": alg, "avg_launch_us": round(t_dec, 2),
+                     "kernel_hash": khash},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

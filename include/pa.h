@@ -1,0 +1,190 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged decode-attention library, libpa.so.
+ *
+ * The operation is PagedAttention decode: one query token per sequence attends
+ * to that sequence's keys and values, which live in fixed-size physical blocks
+ * of a shared pool and are found through the sequence's block table.
+ *
+ * Sources (page title, section):
+ *   [P2] "vLLM deployment and PagedAttention" (crazysre.cn), "Core concept":
+ *        KV cache cut into blocks of block_size tokens; a per-request block
+ *        table maps logical blocks to non-contiguous physical blocks, and
+ *        requests with a common prefix may share physical blocks.
+ *   [P3] "vLLM 0.5 deep dive: PagedAttention architecture" (chenxutan.com):
+ *        s2.1 block pool and allocation, s2.2 the attention interface
+ *        forward(query, key_cache, value_cache, block_table, seq_lens) with
+ *        scale = head_dim^-0.5, s2.3 the kernel's argument list (query,
+ *        key_cache, value_cache, int block_tables, output, scale, ...) and its
+ *        max/sum softmax state, s3.4 FP8 KV cache with a scale and zero point 0.
+ *   [P1] "vLLM 0.7.2 deep dive: PagedAttention v2 with FlashAttention-3"
+ *        (jsqmd.com): s2.1 physical blocks shared by several sequences,
+ *        s2.2 grouped-query heads and the fp8_e4m3 KV cache, s2.3 the 4K
+ *        sliding window (mask keys outside it; never load blocks wholly
+ *        outside it).
+ *
+ * Conventions shared by every entry point
+ *   - All buffer pointers are DEVICE pointers owned by the caller.  The
+ *     library allocates nothing, keeps no state and is reentrant.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call validates its arguments on the host, enqueues its kernels on
+ *     `stream` and returns without synchronising.  Validation happens before
+ *     any HIP call, so an invalid call never touches the device.
+ *   - query, out, both caches, key/value and part_out must be 16-byte aligned
+ *     (PA_ERR_ALIGN otherwise); int32 arrays need only their natural alignment.
+ *   - Return value: a pa_status.  PA_ERR_HIP reports a failed launch
+ *     (hipGetLastError); pa_last_hip_error() gives its text.
+ *   - dtype arguments take a pa_dtype.  Supported (query, KV) pairs:
+ *     (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).  bf16 and f32 outputs are
+ *     rounded to nearest even from fp32.
+ *   - GQA: G = num_q_heads / num_kv_heads; query head h reads KV head h / G.
+ *     Supported: head_dim in {64, 128}, block_size in {16, 32},
+ *     G in {1, 2, 4, 8} for every KV dtype and G = 16 for bf16 / FP8 KV.
+ *
+ * Layouts (element = one cache entry; X = 16 / element bytes, so one X-group
+ * is 16 bytes: X = 4 for f32, 8 for bf16, 16 for FP8):
+ *   query, out      [num_seqs][num_q_heads][head_dim]
+ *   value_cache     [num_blocks][num_kv_heads][head_dim][block_size]
+ *                   -- the order of [P3 s2.2]; element (b,h,d,o) at
+ *                   ((b*Hkv + h)*D + d)*bs + o.
+ *   key_cache       [num_blocks][num_kv_heads][head_dim/X][block_size][X]
+ *                   -- [P3 s2.2]'s order with head_dim cut into 16-byte
+ *                   groups stored innermost; element (b,h,d,o) at
+ *                   (((b*Hkv + h)*(D/X) + d/X)*bs + o)*X + d%X.
+ *                   Each (block, head) tile of either cache is D*bs
+ *                   contiguous elements.
+ *   block_tables    int32 [num_seqs][max_blocks_per_seq]; logical block i of
+ *                   sequence s lives in physical block block_tables[s][i].
+ *   seq_lens        int32 [num_seqs]; keys of sequence s are positions
+ *                   0..seq_lens[s]-1 and its query is position seq_lens[s]-1.
+ *
+ * Device-data preconditions (not checked on the host: the data lives on the
+ * device):
+ *   0 <= seq_lens[s] <= max_blocks_per_seq * block_size; table entries the
+ *   call reads (logical blocks holding in-window keys) lie in [0, num_blocks).
+ *   Entries past the last block or wholly before the window may hold
+ *   anything (e.g. -1) and are never read.  Out-of-range lengths are clamped
+ *   and out-of-range block ids are clamped into the pool, so a violating call
+ *   gives unspecified values but never reads outside the caches.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  PA_ERR_DTYPE = 2,       /* unknown dtype or unsupported (query, KV) pair     */
+  PA_ERR_SHAPE = 3,       /* non-positive size, or num_q_heads % num_kv_heads  */
+  PA_ERR_UNSUPPORTED = 4, /* head_dim / block_size / group size not built      */
+  PA_ERR_PARTITION = 5,   /* bad partition_size / max_num_partitions           */
+  PA_ERR_HIP = 6,         /* a kernel launch failed                            */
+  PA_ERR_ALIGN = 7        /* a buffer is not 16-byte aligned                   */
+} pa_status;
+
+/*
+ * pa_reshape_and_cache -- append new tokens' K/V into their cache slots.
+ *   [P3 s2.1] places a request's tokens in ceil(n/block_size) blocks; [P2]
+ *   maps them through the block table.  slot_mapping[t] = physical_block *
+ *   block_size + offset, computed by the caller from the table.
+ * key, value     [num_tokens][num_kv_heads][head_dim] elements of kv_dtype
+ *                (for FP8_E4M3 these are already E4M3 codes).
+ * slot_mapping   int32 [num_tokens]; a negative slot skips the token; a slot
+ *                >= num_blocks*block_size is also skipped.
+ * The copy is bit-exact and touches only the named slots.  Non-negative slots
+ * must be distinct (two tokens to one slot leave either one's bytes).
+ * num_tokens = 0 is a valid no-op (key, value and slot_mapping may be NULL).
+ */
+int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
+                         const int32_t* slot_mapping, int num_tokens, int num_kv_heads,
+                         int head_dim, int block_size, int num_blocks, int kv_dtype,
+                         void* stream);
+
+/*
+ * pa_decode -- one query per sequence against its paged K/V, in one pass per
+ * (sequence, KV head) ([P3 s2.2/s2.3], [P1 s2.2/s2.3]).
+ *   For query head h of sequence s, with L = seq_lens[s], G = Hq/Hkv,
+ *   lo = sliding_window > 0 ? max(0, L - sliding_window) : 0:
+ *     s_j = scale * k_scale * sum_d q[d] k_j[d]          for j in [lo, L)
+ *     out = v_scale * sum_j softmax(s)_j v_j             (fp32 accumulation)
+ *   where k_j, v_j are the stored elements of key/value head h/G (E4M3 codes
+ *   decoded to their value).  L = 0 gives a zero row.
+ * query   [num_seqs][num_q_heads][head_dim] of q_dtype; out: same shape and dtype.
+ * scale   the softmax scale as fp32 (normally head_dim^-0.5, [P3 s2.2]).
+ * k_scale, v_scale  per-tensor FP8 dequantisation scales ([P3 s3.4], zero
+ *         point 0); pass 1.0f for f32 / bf16 caches.
+ * sliding_window  0 = off.
+ * out must not alias any input.
+ */
+int pa_decode(const void* query, const void* key_cache, const void* value_cache,
+              const int32_t* block_tables, const int32_t* seq_lens, int block_size, float scale,
+              void* out, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+              int max_blocks_per_seq, int num_blocks, int sliding_window, int q_dtype,
+              int kv_dtype, float k_scale, float v_scale, void* stream);
+
+/*
+ * pa_decode_split -- the same attention cut into partitions of partition_size
+ * logical tokens (partition p covers [p*P, (p+1)*P) intersected with
+ * [lo, L)); each partition is normalised on its own and reports its
+ * log-sum-exp, so that pa_reduce_lse can merge them.
+ * partition_size      a multiple of block_size (and of 16), > 0.
+ * max_num_partitions  >= ceil(max_blocks_per_seq * block_size / partition_size).
+ * part_out  fp32 [num_seqs][num_q_heads][max_num_partitions][head_dim]:
+ *           softmax-weighted V of the partition (already divided by its sum).
+ * part_lse  fp32 [num_seqs][num_q_heads][max_num_partitions]: natural-log
+ *           log-sum-exp of the partition's scaled scores s_j.
+ * For an empty partition part_lse is -inf and part_out is not written.
+ * Both buffers together are pa_decode_split_workspace_bytes(...) bytes.
+ */
+int pa_decode_split(const void* query, const void* key_cache, const void* value_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens, int block_size,
+                    float scale, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                    int max_blocks_per_seq, int num_blocks, int sliding_window, int q_dtype,
+                    int kv_dtype, float k_scale, float v_scale, int partition_size,
+                    int max_num_partitions, float* part_out, float* part_lse, void* stream);
+
+/*
+ * pa_reduce_lse -- merge the partitions written by pa_decode_split:
+ *   M = max_p lse_p;  out = sum_p e^(lse_p - M) o_p / sum_p e^(lse_p - M)
+ * over the non-empty partitions of each row (found from seq_lens,
+ * partition_size and sliding_window; the others are not read).  A row with
+ * L = 0 gets zeros.  out: [num_seqs][num_q_heads][head_dim] of out_dtype
+ * (F32 or BF16).
+ */
+int pa_reduce_lse(const float* part_out, const float* part_lse, const int32_t* seq_lens,
+                  int num_seqs, int num_q_heads, int head_dim, int partition_size,
+                  int max_num_partitions, int sliding_window, void* out, int out_dtype,
+                  void* stream);
+
+/* Bytes of part_out + part_lse for pa_decode_split (part_lse starts at
+   offset num_seqs*num_q_heads*max_num_partitions*head_dim*4). */
+size_t pa_decode_split_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
+                                       int max_num_partitions);
+
+/*
+ * pa_fp8_e4m3_dequantize -- out[i] = value(codes[i]) * scale for i < n, with
+ * the same device conversion of OCP E4M3 codes that the decode kernels use
+ * ([P1 s2.2] fp8_e4m3 cache, [P3 s3.4] scale with zero point 0).  codes need
+ * no alignment; out must be 16-byte aligned.  n = 0 is a no-op.
+ */
+int pa_fp8_e4m3_dequantize(const uint8_t* codes, float scale, float* out, long long n,
+                           void* stream);
+
+/* Human-readable name of a pa_status. */
+const char* pa_status_string(int status);
+
+/* Text of the last HIP error seen by this thread (empty if none). */
+const char* pa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

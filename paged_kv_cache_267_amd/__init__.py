@@ -1,0 +1,186 @@
+"""Python binding of libpa.so, the MI355X paged decode-attention library.
+
+The functions below carry the names of the C ABI in ``include/pa.h`` and do
+argument marshalling only: every step runs in the library's HIP kernels.
+torch provides device memory and the stream (``torch.cuda.current_stream()``
+unless a stream is passed).  If libpa.so has not been built, the first call
+raises ``PaLibraryMissing``; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE",
+          4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_PARTITION", 6: "PA_ERR_HIP", 7: "PA_ERR_ALIGN"}
+
+# exported symbols (include/pa.h)
+EXPORTS = ("pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_reduce_lse",
+           "pa_decode_split_workspace_bytes", "pa_fp8_e4m3_dequantize", "pa_status_string",
+           "pa_last_hip_error")
+
+
+class PaLibraryMissing(ImportError):
+    pass
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libpa.so (raises PaLibraryMissing if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise PaLibraryMissing(
+            f"{LIB_PATH} is not built; run `python -m paged_kv_cache_267_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.pa_reshape_and_cache.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
+    L.pa_decode.argtypes = [P, P, P, P, P, I, F, P, I, I, I, I, I, I, I, I, I, F, F, P]
+    L.pa_decode_split.argtypes = [P, P, P, P, P, I, F, I, I, I, I, I, I, I, I, I, F, F, I, I, P,
+                                  P, P]
+    L.pa_reduce_lse.argtypes = [P, P, P, I, I, I, I, I, I, P, I, P]
+    L.pa_decode_split_workspace_bytes.argtypes = [I, I, I, I]
+    L.pa_decode_split_workspace_bytes.restype = ctypes.c_size_t
+    L.pa_fp8_e4m3_dequantize.argtypes = [P, F, P, ctypes.c_longlong, P]
+    L.pa_status_string.argtypes = [I]
+    L.pa_status_string.restype = ctypes.c_char_p
+    L.pa_last_hip_error.argtypes = []
+    L.pa_last_hip_error.restype = ctypes.c_char_p
+    for name in ("pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_reduce_lse",
+                 "pa_fp8_e4m3_dequantize"):
+        getattr(L, name).restype = I
+    _lib = L
+    return L
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        L = lib()
+        msg = L.pa_status_string(rc).decode()
+        if rc == 6:
+            msg += f" ({L.pa_last_hip_error().decode()})"
+        raise PaError(rc, msg)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PA_FP8_E4M3
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _num_blocks(cache, num_kv_heads, head_dim, block_size) -> int:
+    per_block = num_kv_heads * head_dim * block_size
+    assert cache.numel() % per_block == 0, "cache size is not a whole number of blocks"
+    return cache.numel() // per_block
+
+
+def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, *, block_size,
+                         stream=None) -> None:
+    """Write key/value [T, Hkv, D] into their slots of the paged caches."""
+    T, Hkv, D = key.shape
+    assert value.shape == key.shape and slot_mapping.shape[0] == T
+    _check(lib().pa_reshape_and_cache(
+        _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping), T, Hkv,
+        D, block_size, _num_blocks(key_cache, Hkv, D, block_size), _dtype_code(key_cache),
+        _stream(stream)))
+
+
+def pa_decode(query, key_cache, value_cache, block_tables, seq_lens, *, block_size, scale, out,
+              num_kv_heads, sliding_window=0, k_scale=1.0, v_scale=1.0, stream=None) -> None:
+    """Unsplit decode into ``out`` [S, Hq, D] (query dtype)."""
+    S, Hq, D = query.shape
+    _check(lib().pa_decode(
+        _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables), _ptr(seq_lens),
+        block_size, float(scale), _ptr(out), S, Hq, num_kv_heads, D, block_tables.shape[1],
+        _num_blocks(key_cache, num_kv_heads, D, block_size), int(sliding_window),
+        _dtype_code(query), _dtype_code(key_cache), float(k_scale), float(v_scale),
+        _stream(stream)))
+
+
+def pa_decode_split(query, key_cache, value_cache, block_tables, seq_lens, *, block_size, scale,
+                    num_kv_heads, partition_size, max_num_partitions, part_out, part_lse,
+                    sliding_window=0, k_scale=1.0, v_scale=1.0, stream=None) -> None:
+    """Split decode: per-partition outputs [S, Hq, P, D] and LSEs [S, Hq, P] (fp32)."""
+    S, Hq, D = query.shape
+    _check(lib().pa_decode_split(
+        _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables), _ptr(seq_lens),
+        block_size, float(scale), S, Hq, num_kv_heads, D, block_tables.shape[1],
+        _num_blocks(key_cache, num_kv_heads, D, block_size), int(sliding_window),
+        _dtype_code(query), _dtype_code(key_cache), float(k_scale), float(v_scale),
+        int(partition_size), int(max_num_partitions), _ptr(part_out), _ptr(part_lse),
+        _stream(stream)))
+
+
+def pa_reduce_lse(part_out, part_lse, seq_lens, *, partition_size, sliding_window=0, out,
+                  stream=None) -> None:
+    """Merge partitions into ``out`` [S, Hq, D] (float32 or bfloat16)."""
+    S, Hq, P, D = part_out.shape
+    _check(lib().pa_reduce_lse(
+        _ptr(part_out), _ptr(part_lse), _ptr(seq_lens), S, Hq, D, int(partition_size), P,
+        int(sliding_window), _ptr(out), _dtype_code(out), _stream(stream)))
+
+
+def pa_decode_split_workspace_bytes(num_seqs, num_q_heads, head_dim, max_num_partitions) -> int:
+    return int(lib().pa_decode_split_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                     max_num_partitions))
+
+
+def pa_fp8_e4m3_dequantize(codes, scale, out, stream=None) -> None:
+    """out[i] = value(codes[i]) * scale with the kernels' device conversion."""
+    _check(lib().pa_fp8_e4m3_dequantize(_ptr(codes), float(scale), _ptr(out), codes.numel(),
+                                        _stream(stream)))
+
+
+def decode(query, key_cache, value_cache, block_tables, seq_lens, *, block_size, scale,
+           num_kv_heads, sliding_window=0, k_scale=1.0, v_scale=1.0, partition_size=None,
+           out=None, stream=None):
+    """Decode attention; unsplit if partition_size is None, else split + LSE merge
+    (the fp32 workspace is allocated through torch)."""
+    import torch
+    S, Hq, D = query.shape
+    if out is None:
+        out = torch.empty_like(query)
+    if partition_size is None:
+        pa_decode(query, key_cache, value_cache, block_tables, seq_lens, block_size=block_size,
+                  scale=scale, out=out, num_kv_heads=num_kv_heads, sliding_window=sliding_window,
+                  k_scale=k_scale, v_scale=v_scale, stream=stream)
+        return out
+    P = max(1, -(-block_tables.shape[1] * block_size // partition_size))
+    part_out = torch.empty((S, Hq, P, D), dtype=torch.float32, device=query.device)
+    part_lse = torch.empty((S, Hq, P), dtype=torch.float32, device=query.device)
+    pa_decode_split(query, key_cache, value_cache, block_tables, seq_lens, block_size=block_size,
+                    scale=scale, num_kv_heads=num_kv_heads, partition_size=partition_size,
+                    max_num_partitions=P, part_out=part_out, part_lse=part_lse,
+                    sliding_window=sliding_window, k_scale=k_scale, v_scale=v_scale,
+                    stream=stream)
+    pa_reduce_lse(part_out, part_lse, seq_lens, partition_size=partition_size,
+                  sliding_window=sliding_window, out=out, stream=stream)
+    return out

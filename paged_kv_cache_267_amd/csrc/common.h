@@ -1,0 +1,110 @@
+// common.h -- device helpers shared by the gfx950 kernels of libpa.so.
+//
+// Wave64 cross-lane primitives (DPP within a 16-lane row, swaps across rows),
+// bf16 / E4M3 element handling, and the parameter block of the decode kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
+
+// Element bytes of a cache entry; a 16-byte group holds 16 / bytes elements.
+template <int KV> struct KvTraits;
+template <> struct KvTraits<KV_F32> { static constexpr int E = 4; };
+template <> struct KvTraits<KV_BF16> { static constexpr int E = 2; };
+template <> struct KvTraits<KV_FP8> { static constexpr int E = 1; };
+
+// Parameters of one decode launch (unsplit when part_out == nullptr).
+struct DecodeParams {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  void* out;            // unsplit output [S][Hq][D], query dtype
+  float* part_out;      // split: [S][Hq][max_parts][D]
+  float* part_lse;      // split: [S][Hq][max_parts]
+  float qk_scale;       // scale * k_scale * log2(e): scores in base-2 units
+  float v_scale;
+  int num_seqs, num_q_heads, num_kv_heads;
+  int max_blocks, num_blocks, window;
+  int partition_size;   // tokens per partition (split); 0 = whole sequence
+  int max_parts;
+};
+
+// ---- scalar conversions ------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair (round to nearest even), lo in bits 0..15.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t to_bf16_bits(float x) {
+  return (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu);
+}
+
+// Two E4M3 codes (bytes 0,1 or 2,3 of w) -> packed bf16 pair; exact.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// bf16x2 dot product accumulated in fp32: a.lo*b.lo + a.hi*b.hi + c.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- cross-lane --------------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+
+// All-reduce over each 16-lane row.
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp<DPP_XOR1>(x));
+  x = fmaxf(x, dpp<DPP_XOR2>(x));
+  x = fmaxf(x, dpp<DPP_ROW_HALF_MIRROR>(x));
+  x = fmaxf(x, dpp<DPP_ROW_MIRROR>(x));
+  return x;
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp<DPP_XOR1>(x);
+  x += dpp<DPP_XOR2>(x);
+  x += dpp<DPP_ROW_HALF_MIRROR>(x);
+  x += dpp<DPP_ROW_MIRROR>(x);
+  return x;
+}
+
+// Value held by lane (lane ^ 32) / (lane ^ 16).
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+__device__ __forceinline__ float xor16(float x) { return __shfl_xor(x, 16, 64); }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+}  // namespace pa

@@ -1,0 +1,37 @@
+// dispatch.h -- host-side entry points of the kernel instances.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace pa {
+
+// Waves per workgroup of the VALU decode kernel.
+constexpr int VALU_WAVES = 4;
+
+// VALU (bandwidth) path, one function per KV element type; they switch over
+// (head_dim, block_size, group) and return hipErrorInvalidValue for a
+// combination that is not instantiated.
+hipError_t decode_valu_f32(const DecodeParams& p, int D, int BS, int G, int parts, int waves,
+                           hipStream_t stream);
+hipError_t decode_valu_bf16(const DecodeParams& p, int D, int BS, int G, int parts, int waves,
+                            hipStream_t stream);
+hipError_t decode_valu_fp8(const DecodeParams& p, int D, int BS, int G, int parts, int waves,
+                           hipStream_t stream);
+
+// Chooses the kernel family for (KV dtype, group size) and launches it with a
+// grid of (num_kv_heads, parts, num_seqs).
+hipError_t dispatch_decode(const DecodeParams& p, int kv_dtype, int D, int BS, int G, int parts,
+                           hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc, void* vc,
+                                    const int32_t* slots, int T, int Hkv, int D, int bs,
+                                    int num_blocks, int elem_bytes, hipStream_t stream);
+hipError_t launch_reduce_lse(const float* part_out, const float* part_lse,
+                             const int32_t* seq_lens, int S, int Hq, int D, int P, int max_parts,
+                             int window, void* out, bool out_bf16, hipStream_t stream);
+hipError_t launch_fp8_dequant(const uint8_t* codes, float scale, float* out, long long n,
+                              hipStream_t stream);
+
+}  // namespace pa

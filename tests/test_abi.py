@@ -1,0 +1,124 @@
+"""The C ABI on a host without a GPU: the library loads, exports every symbol
+include/pa.h declares, and rejects invalid calls before any HIP call."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_267_amd as pa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "pa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_what_the_binding_knows():
+    assert declared_functions() == sorted(pa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = pa.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+# fake, 16-byte aligned, never dereferenced addresses
+A = ctypes.c_void_p(0x10000)
+B = ctypes.c_void_p(0x20000)
+ODD = ctypes.c_void_p(0x20008)
+NULL = ctypes.c_void_p(0)
+
+
+def dec(**kw):
+    args = dict(q=A, kc=A, vc=A, bt=A, sl=A, bs=16, scale=0.125, out=B, S=2, Hq=8, Hkv=2, D=128,
+                mb=4, nb=8, win=0, qdt=1, kvdt=1, ks=1.0, vs=1.0, stream=NULL)
+    args.update(kw)
+    return pa.lib().pa_decode(*args.values())
+
+
+def split(**kw):
+    args = dict(q=A, kc=A, vc=A, bt=A, sl=A, bs=16, scale=0.125, S=2, Hq=8, Hkv=2, D=128, mb=4,
+                nb=8, win=0, qdt=1, kvdt=1, ks=1.0, vs=1.0, P=32, maxp=2, po=B, pl=B,
+                stream=NULL)
+    args.update(kw)
+    return pa.lib().pa_decode_split(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), 1), (dict(bt=NULL), 1), (dict(out=NULL), 1),
+    (dict(qdt=0, kvdt=1), 2), (dict(qdt=1, kvdt=0), 2), (dict(qdt=2, kvdt=2), 2),
+    (dict(kvdt=9), 2),
+    (dict(S=-1), 3), (dict(Hq=0), 3), (dict(Hq=6, Hkv=4), 3), (dict(mb=0), 3), (dict(nb=0), 3),
+    (dict(win=-1), 3), (dict(scale=float("nan")), 3), (dict(S=70000), 3),
+    (dict(D=96), 4), (dict(bs=8), 4), (dict(bs=64), 4), (dict(Hq=6, Hkv=2), 4),
+    (dict(Hq=64, Hkv=2), 4),
+    (dict(out=ODD), 7), (dict(q=ODD), 7),
+])
+def test_decode_validation(kw, status):
+    assert dec(**kw) == status
+
+
+def test_decode_empty_batch_is_a_noop():
+    assert dec(S=0) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(po=NULL), 1), (dict(pl=NULL), 1),
+    (dict(P=0), 5), (dict(P=24), 5), (dict(maxp=1), 5), (dict(maxp=0), 5),
+    (dict(po=ODD), 7),
+])
+def test_split_validation(kw, status):
+    assert split(**kw) == status
+
+
+def test_reshape_and_cache_validation():
+    L = pa.lib()
+    ok = [A, A, A, A, A, 4, 2, 128, 16, 8, 1, NULL]
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return L.pa_reshape_and_cache(*a)
+    assert call(0, NULL) == 1
+    assert call(4, NULL) == 1
+    assert call(2, NULL) == 1
+    assert call(10, 5) == 2
+    assert call(5, -1) == 3
+    assert call(7, 100) == 4
+    assert call(8, 24) == 4
+    assert call(0, ODD) == 7
+    assert call(5, 0) == 0  # zero tokens: no-op
+    a = list(ok); a[0] = a[1] = a[4] = NULL; a[5] = 0
+    assert L.pa_reshape_and_cache(*a) == 0
+
+
+def test_reduce_validation():
+    L = pa.lib()
+    ok = [A, A, A, 2, 8, 128, 32, 4, 0, B, 1, NULL]
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return L.pa_reduce_lse(*a)
+    assert call(0, NULL) == 1
+    assert call(10, 2) == 2
+    assert call(4, 0) == 3
+    assert call(5, 80) == 4
+    assert call(6, 0) == 5
+    assert call(9, ODD) == 7
+    assert call(3, 0) == 0
+
+
+def test_workspace_bytes():
+    assert pa.pa_decode_split_workspace_bytes(3, 8, 128, 5) == 3 * 8 * 5 * (128 + 1) * 4
+    assert pa.pa_decode_split_workspace_bytes(0, 8, 128, 5) == 0
+
+
+def test_status_strings():
+    for s in range(8):
+        assert pa.lib().pa_status_string(s)

@@ -1,0 +1,284 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bars (written here, derived in the design notes):
+  - reshape_and_cache: bit-exact, whole caches.
+  - bf16 KV: max abs <= 1e-2 and mean abs <= 1e-3.
+  - fp8_e4m3 KV: max abs <= 2e-2 against the oracle fed the same codes and scales.
+  - f32 KV (all-fp32 path): max abs <= 1e-4.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_267_amd import workloads as W
+from tests.helpers import err_stats, oracle_caches, oracle_decode, oracle_decode_split
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": (1e-2, 1e-3), "fp8_e4m3": (2e-2, 2e-3), "f32": (1e-4, 1e-5)}
+
+
+def announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def gpu_run(wl, *, split, partition_size=None):
+    import torch
+    from paged_kv_cache_267_amd.harness import DeviceWorkload
+    dw = DeviceWorkload(wl, partition_size=partition_size)
+    dw.fill_history()
+    dw.step(split=split)
+    torch.cuda.synchronize()
+    return dw
+
+
+def assert_close(got, ref, kv_dtype, what):
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    mx, mean = err_stats(got, ref)
+    tmax, tmean = TOL[kv_dtype]
+    print(f"    {what}: max abs {mx:.3e} mean abs {mean:.3e}", flush=True)
+    assert mx <= tmax and mean <= tmean, f"{what}: max {mx:.3e} mean {mean:.3e}"
+
+
+# ---------------------------------------------------------------------------
+# FP8 conversion on the device: all 256 codes
+
+def test_fp8_device_conversion_all_codes():
+    import torch
+    import paged_kv_cache_267_amd as pa
+    announce("fp8 conversion, 256 codes")
+    codes = torch.arange(256, dtype=torch.uint8, device="cuda")
+    out = torch.empty(256, dtype=torch.float32, device="cuda")
+    pa.pa_fp8_e4m3_dequantize(codes, 1.0, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    ref = oracle.fp8_e4m3_value(np.arange(256, dtype=np.uint8))
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    # with a scale: value * scale rounded once to fp32
+    pa.pa_fp8_e4m3_dequantize(codes, 0.0123, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref32 = (ref * np.float64(np.float32(0.0123))).astype(np.float32)
+    assert np.array_equal(got[ok], ref32[ok])
+
+
+# ---------------------------------------------------------------------------
+# reshape_and_cache: bit-exact against the oracle's cache
+
+@pytest.mark.parametrize("kvdt,D,bs", [("f32", 64, 16), ("bf16", 128, 16), ("bf16", 128, 32),
+                                       ("bf16", 64, 32), ("fp8_e4m3", 128, 16)])
+def test_reshape_and_cache_bit_exact(kvdt, D, bs):
+    announce(f"reshape_and_cache {kvdt} D{D} bs{bs}")
+    qdt = "f32" if kvdt == "f32" else "bf16"
+    wl = W.random_case(21, seq_lens=[1, 15, 16, 17, 100, 257], num_q_heads=4, num_kv_heads=2,
+                       head_dim=D, block_size=bs, q_dtype=qdt, kv_dtype=kvdt)
+    dw = gpu_run(wl, split=False)
+    gk, gv = dw.cache_bytes()
+    kc, vc = oracle_caches(wl)
+    assert np.array_equal(gk, kc.view(np.uint8))
+    assert np.array_equal(gv, vc.view(np.uint8))
+
+
+def test_reshape_and_cache_skips_negative_and_out_of_pool_slots():
+    import torch
+    import paged_kv_cache_267_amd as pa
+    announce("reshape_and_cache skip rules")
+    T, H, D, bs, NB = 6, 2, 128, 16, 4
+    g = torch.Generator().manual_seed(0)
+    key = torch.randn(T, H, D, generator=g).to(torch.bfloat16).cuda()
+    val = torch.randn(T, H, D, generator=g).to(torch.bfloat16).cuda()
+    slots = torch.tensor([0, -1, 5, NB * bs, 63, -7], dtype=torch.int32).cuda()
+    kc = torch.full((NB * H * D * bs * 2,), 0xAB, dtype=torch.uint8).cuda().view(torch.bfloat16)
+    vc = kc.clone()
+    pa.pa_reshape_and_cache(key, val, kc, vc, slots, block_size=bs)
+    torch.cuda.synchronize()
+    ok = np.array([0, 5, 63])
+    kc_o = np.full(NB * H * D * bs, 0xABAB, np.uint16)
+    vc_o = kc_o.copy()
+    kh = key.cpu().view(torch.int16).numpy().view(np.uint16)
+    vh = val.cpu().view(torch.int16).numpy().view(np.uint16)
+    sl = np.array([0, -1, 5, NB * bs, 63, -7], np.int32)
+    sl[[1, 3, 5]] = -1
+    oracle.reshape_and_cache(kh, vh, kc_o, vc_o, sl, num_kv_heads=H, head_dim=D, block_size=bs,
+                             num_blocks=NB, kv_dtype="bf16")
+    assert np.array_equal(kc.cpu().view(torch.int16).numpy().view(np.uint16), kc_o)
+    assert np.array_equal(vc.cpu().view(torch.int16).numpy().view(np.uint16), vc_o)
+    assert len(ok) == 3
+
+
+# ---------------------------------------------------------------------------
+# decode parity on small cases spanning several tiles and ragged tails
+
+SMALL = []
+for kvdt in ("f32", "bf16", "fp8_e4m3"):
+    for D in (64, 128):
+        for bs in (16, 32):
+            for G in (1, 2, 4, 8):
+                SMALL.append((kvdt, D, bs, G))
+
+
+@pytest.mark.parametrize("kvdt,D,bs,G", SMALL)
+@pytest.mark.parametrize("split", [False, True])
+def test_decode_small_parity(kvdt, D, bs, G, split):
+    qdt = "f32" if kvdt == "f32" else "bf16"
+    window = 0 if G != 2 else 70
+    lens = [0, 1, 2, 15, 16, 17, 33, 100, 129, 300]
+    announce(f"decode {kvdt} D{D} bs{bs} G{G} split={split} window={window}")
+    wl = W.random_case(1000 + D + bs + G, seq_lens=lens, num_q_heads=2 * G, num_kv_heads=2,
+                       head_dim=D, block_size=bs, q_dtype=qdt, kv_dtype=kvdt,
+                       sliding_window=window, partition_size=64)
+    dw = gpu_run(wl, split=split)
+    kc, vc = oracle_caches(wl)
+    ref = oracle_decode(wl, kc, vc)
+    assert_close(dw.out_f64(), ref, kvdt, "out")
+    # L = 0 rows are exact zeros
+    L = np.repeat(wl.seq_lens, wl.num_q_heads)
+    assert np.all(dw.out_f64()[L == 0] == 0.0)
+
+
+@pytest.mark.parametrize("kvdt", ["bf16", "fp8_e4m3"])
+def test_split_partials_and_lse(kvdt):
+    import torch
+    announce(f"split partials {kvdt}")
+    wl = W.random_case(77, seq_lens=[0, 5, 64, 65, 200, 513], num_q_heads=8, num_kv_heads=2,
+                       head_dim=128, block_size=16, kv_dtype=kvdt, sliding_window=150,
+                       partition_size=64)
+    dw = gpu_run(wl, split=True)
+    kc, vc = oracle_caches(wl)
+    po, pl = oracle_decode_split(wl, kc, vc, max_partitions=dw.max_parts)
+    g_lse = dw.part_lse.cpu().numpy().reshape(pl.shape).astype(np.float64)
+    g_po = dw.part_out.cpu().numpy().reshape(po.shape).astype(np.float64)
+    empty = np.isneginf(pl)
+    assert np.array_equal(np.isneginf(g_lse), empty)
+    np.testing.assert_allclose(g_lse[~empty], pl[~empty], rtol=0, atol=1e-4)
+    mx, _ = err_stats(g_po[~empty], po[~empty])
+    assert mx <= 1e-2
+    del torch
+
+
+# ---------------------------------------------------------------------------
+# invariants on the device
+
+def test_gpu_block_permutation_bit_identical():
+    import torch
+    announce("gpu permutation invariance")
+    wl = W.random_case(31, seq_lens=[3, 50, 77, 200], num_q_heads=8, num_kv_heads=2,
+                       head_dim=128, block_size=16)
+    a = gpu_run(wl, split=True).out.clone()
+    # same logical content, physical ids relabelled by a permutation of the pool
+    pi = np.random.default_rng(8).permutation(wl.num_blocks).astype(np.int32)
+    bs = wl.block_size
+    relabel = lambda sl: (pi[sl // bs] * bs + sl % bs).astype(np.int32)
+    t2 = np.where(wl.block_tables >= 0, pi[np.maximum(wl.block_tables, 0)], -1).astype(np.int32)
+    wl2 = dataclasses.replace(wl, block_tables=t2, hist_slots=relabel(wl.hist_slots),
+                              new_slots=relabel(wl.new_slots))
+    b = gpu_run(wl2, split=True).out
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_gpu_prefix_aliasing_bit_identical():
+    import torch
+    announce("gpu prefix aliasing invariance")
+    wl = W.random_case(32, seq_lens=[40, 57, 33, 90], num_q_heads=8, num_kv_heads=2,
+                       head_dim=128, block_size=16, shared_prefix=32)
+    a = gpu_run(wl, split=False).out.clone()
+    # give every sequence after the first its own copy of the prefix blocks
+    spare = wl.num_blocks
+    t2 = wl.block_tables.copy()
+    hist_k, hist_v, hist_s = [wl.hist_key], [wl.hist_value], [wl.hist_slots]
+    pfx = wl.block_tables[0, :2]
+    pfx_slots = (pfx[:, None] * 16 + np.arange(16)[None, :]).ravel()
+    idx = np.array([int(np.nonzero(wl.hist_slots == s)[0][0]) for s in pfx_slots])
+    for s in range(1, wl.num_seqs):
+        new_ids = np.array([spare, spare + 1], np.int32)
+        spare += 2
+        t2[s, :2] = new_ids
+        hist_k.append(wl.hist_key[idx])
+        hist_v.append(wl.hist_value[idx])
+        hist_s.append((new_ids[:, None] * 16 + np.arange(16)[None, :]).ravel().astype(np.int32))
+    wl2 = dataclasses.replace(wl, block_tables=t2, num_blocks=spare,
+                              hist_key=np.concatenate(hist_k), hist_value=np.concatenate(hist_v),
+                              hist_slots=np.concatenate(hist_s))
+    b = gpu_run(wl2, split=False).out
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("kvdt", ["f32", "bf16"])
+def test_gpu_len_one_and_window_one_exact(kvdt):
+    announce(f"closed forms {kvdt}")
+    qdt = "f32" if kvdt == "f32" else "bf16"
+    wl = W.random_case(41, seq_lens=[1, 1, 1, 1], num_q_heads=4, num_kv_heads=2, head_dim=128,
+                       block_size=16, q_dtype=qdt, kv_dtype=kvdt)
+    kc, vc = oracle_caches(wl)
+    for split in (False, True):
+        got = gpu_run(wl, split=split).out_f64()
+        assert np.array_equal(got, oracle_decode(wl, kc, vc)), "L = 1 must return V row 0"
+    wl = W.random_case(42, seq_lens=[5, 16, 40, 99], num_q_heads=4, num_kv_heads=2, head_dim=128,
+                       block_size=16, q_dtype=qdt, kv_dtype=kvdt, sliding_window=1)
+    kc, vc = oracle_caches(wl)
+    for split in (False, True):
+        got = gpu_run(wl, split=split).out_f64()
+        assert np.array_equal(got, oracle_decode(wl, kc, vc)), "W = 1 must return V row L-1"
+
+
+def test_window_skips_blocks_before_window():
+    announce("window tile skip with NaN-poisoned out-of-window blocks")
+    wl = W.random_case(51, seq_lens=[300, 33, 1000, 4], num_q_heads=8, num_kv_heads=2,
+                       head_dim=128, block_size=16, kv_dtype="fp8_e4m3", sliding_window=100,
+                       poison_out_of_window=True)
+    kc, vc = oracle_caches(wl)
+    ref = oracle_decode(wl, kc, vc)
+    for split in (False, True):
+        assert_close(gpu_run(wl, split=split).out_f64(), ref, "fp8_e4m3", f"split={split}")
+
+
+# ---------------------------------------------------------------------------
+# the five named workloads at full size
+
+def _rows_sample(wl, n, seed=0):
+    total = wl.num_seqs * wl.num_q_heads
+    if n >= total:
+        return None
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(total, size=n, replace=False).tolist())
+    # always include every head of the longest sequence
+    s = int(np.argmax(wl.seq_lens))
+    rows |= set(range(s * wl.num_q_heads, (s + 1) * wl.num_q_heads))
+    return np.array(sorted(rows), dtype=np.int32)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_named_config_parity(cfg):
+    announce(f"config {cfg}: generating")
+    wl = W.config(cfg)
+    split = cfg != 1
+    announce(f"config {cfg} ({wl.name}): gpu step split={split}")
+    dw = gpu_run(wl, split=split)
+    got = dw.out_f64()
+    announce(f"config {cfg}: oracle")
+    rows = _rows_sample(wl, 4096 if cfg in (3, 5) else 1 << 30)
+    kc, vc = oracle_caches(wl)
+    ref = oracle_decode(wl, kc, vc, rows=rows)
+    if rows is not None:
+        got = got[rows]
+    assert_close(got, ref, wl.kv_dtype, f"config {cfg}")
+    if cfg == 4:  # the appended token went where the oracle put it
+        gk, gv = dw.cache_bytes()
+        assert np.array_equal(gk, kc.view(np.uint8)) and np.array_equal(gv, vc.view(np.uint8))
+
+
+def test_config5_window_poison_variant():
+    announce("config 5 with out-of-window blocks pointing at a NaN block")
+    wl = W.config(5, poison_out_of_window=True)
+    dw = gpu_run(wl, split=True)
+    rows = _rows_sample(wl, 2048, seed=1)
+    kc, vc = oracle_caches(wl)
+    assert_close(dw.out_f64()[rows], oracle_decode(wl, kc, vc, rows=rows), "fp8_e4m3", "cfg5-skip")
