@@ -74,6 +74,24 @@ def load_traffic(kernel_hash: str, workload: str, mode: str):
     return r.get("bytes_per_launch")
 
 
+def read_ceiling(gib: int = 2, reps: int = 10):
+    """Achievable streaming-read bandwidth on this GPU: a full reduction
+    (torch.sum) over a fresh 2 GiB fp32 tensor, averaged over reps calls."""
+    import torch
+    x = torch.ones((gib << 30) // 4, dtype=torch.float32, device="cuda")
+    torch.sum(x)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        torch.sum(x)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    del x
+    return {"GB/s": round((gib << 30) / (us * 1e-6) / 1e9, 1), "probe": "torch.sum over 2 GiB fp32"}
+
+
 def cpu_baseline(wl, budget_s: float):
     """The oracle as it stands, on the host cores, over the whole workload;
     repeated until at least budget_s seconds of work (at least once)."""
@@ -103,6 +121,10 @@ def main():
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a reference "
+                         "kernel of known traffic for hardware-counter scaling)")
+    ap.add_argument("--no-ceiling", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -124,6 +146,16 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] {wl.name}: {wl.description}; mode={args.mode} partition={psize}",
           file=sys.stderr, flush=True)
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    ceiling = None if args.no_ceiling else read_ceiling()
 
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -180,8 +212,11 @@ def main():
                      "traffic": traffic, "kernel": "decode_valu_kernel",
                      "algorithmic_bytes_per_launch": alg, "avg_launch_us": round(t_dec, 2),
                      "kernel_hash": khash},
+        "read_ceiling": ceiling,
         "cpu_baseline": None,
     }
+    if ceiling:
+        rec["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling["GB/s"], 4)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)

@@ -31,8 +31,8 @@ bool valid_pair(int q_dtype, int kv_dtype) {
 }
 
 bool group_supported(int kv_dtype, int G) {
-  (void)kv_dtype;
-  return G == 1 || G == 2 || G == 4 || G == 8;
+  if (G == 1 || G == 2 || G == 4 || G == 8) return true;
+  return G == 16 && kv_dtype != PA_F32;
 }
 
 // Checks shared by pa_decode and pa_decode_split.

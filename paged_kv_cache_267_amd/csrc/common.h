@@ -12,6 +12,8 @@ namespace pa {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
@@ -66,6 +68,12 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// 16-byte non-temporal global load (streamed data, read once).
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+  const u32x4_t t = __builtin_nontemporal_load((const u32x4_t*)p);
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---- cross-lane --------------------------------------------------------------
@@ -101,9 +109,20 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
-// Value held by lane (lane ^ 32) / (lane ^ 16).
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
-__device__ __forceinline__ float xor16(float x) { return __shfl_xor(x, 16, 64); }
+// Swap-adds across lane rows (v_permlane32_swap / v_permlane16_swap, VALU).
+// swap_add32(a, b): lanes 0..31 get a(l) + a(l+32), lanes 32..63 get
+//   b(l-32) + b(l)  -- the two halves keep different values, fully summed.
+// swap_add16(a, b): rows 0 and 2 (lanes 0-15, 32-47) get a(l) + a(l+16),
+//   rows 1 and 3 get b(l-16) + b(l).
+// With a == b both give the plain sum over the lane pair.
+__device__ __forceinline__ float swap_add32(float a, float b) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_add16(float a, float b) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

@@ -19,7 +19,7 @@
 // The workgroup copies its slice of the block table into LDS, then its waves
 // walk 16-token sub-tiles of the KV range round-robin.  Per sub-tile a wave
 //   - loads the K sub-tile (16 tokens x D) and the V sub-tile with 16-byte
-//     loads, one sub-tile ahead of the one being computed;
+//     non-temporal loads, two sub-tiles ahead of the one being computed;
 //   - lane (row r, column o): token o, 16-byte K groups r, r+4, ... -> partial
 //     dot products for all G query heads of the KV head from one K read;
 //   - folds partials over the 4 rows with two cross-row swap-adds that leave
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(64 * VALU_MAX_WAVES) void decode_valu_kernel(Decode
   const int st_lo = t0 >> 4, st_hi = (t1 + 15) >> 4;
   const int b_lo = st_lo / SPB, b_hi = (st_hi + SPB - 1) / SPB;
 
-  uint4 kb0[KPL], vb0[VPL], kb1[KPL], vb1[VPL];
+  uint4 kb0[KPL], vb0[VPL], kb1[KPL], vb1[VPL], kb2[KPL], vb2[VPL];
 
   auto load_tile = [&](uint4* kb, uint4* vb, int st, int tbl_base) {
     const int blk = st / SPB;
@@ -173,10 +173,12 @@ __global__ __launch_bounds__(64 * VALU_MAX_WAVES) void decode_valu_kernel(Decode
     const int sub = st % SPB;
     const char* kp = kbase + (size_t)phys * block_stride + sub * 256;
     const char* vp = vbase + (size_t)phys * block_stride + sub * 16 * E;
+    // K/V are read once per call: non-temporal loads keep them from evicting
+    // the block table, query and shared-prefix lines from L2
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) kb[i] = *(const uint4*)(kp + koff[i]);
+    for (int i = 0; i < KPL; ++i) kb[i] = load_nt16(kp + koff[i]);
 #pragma unroll
-    for (int k = 0; k < VPL; ++k) vb[k] = *(const uint4*)(vp + voff[k]);
+    for (int k = 0; k < VPL; ++k) vb[k] = load_nt16(vp + voff[k]);
   };
 
   uint32_t* pw = &sm.p[wave][0][0];
@@ -215,30 +217,22 @@ __global__ __launch_bounds__(64 * VALU_MAX_WAVES) void decode_valu_kernel(Decode
       }
     }
     // fold over the 4 rows: lane keeps the heads of its row, fully summed
+    // (lower half keeps heads [0, G/2), upper half [G/2, G); then even rows
+    //  keep the first half of those, odd rows the second)
     float f1[G >= 2 ? G / 2 : 1];
-    const bool upper = lane >= 32;
     if (G >= 2) {
 #pragma unroll
-      for (int k = 0; k < G / 2; ++k) {
-        const float keep = upper ? part_s[k + G / 2] : part_s[k];
-        const float send = upper ? part_s[k] : part_s[k + G / 2];
-        f1[k] = keep + xor32(send);
-      }
+      for (int k = 0; k < G / 2; ++k) f1[k] = swap_add32(part_s[k], part_s[k + G / 2]);
     } else {
-      f1[0] = part_s[0] + xor32(part_s[0]);
+      f1[0] = swap_add32(part_s[0], part_s[0]);
     }
     constexpr int N1 = G >= 2 ? G / 2 : 1;
     float sc[NGL];
-    const bool odd = row & 1;
     if (N1 >= 2) {
 #pragma unroll
-      for (int k = 0; k < N1 / 2; ++k) {
-        const float keep = odd ? f1[k + N1 / 2] : f1[k];
-        const float send = odd ? f1[k] : f1[k + N1 / 2];
-        sc[k] = keep + xor16(send);
-      }
+      for (int k = 0; k < N1 / 2; ++k) sc[k] = swap_add16(f1[k], f1[k + N1 / 2]);
     } else {
-      sc[0] = f1[0] + xor16(f1[0]);
+      sc[0] = swap_add16(f1[0], f1[0]);
     }
 
     // mask and online softmax (base 2)
@@ -357,17 +351,22 @@ __global__ __launch_bounds__(64 * VALU_MAX_WAVES) void decode_valu_kernel(Decode
     __syncthreads();
     const int cs_lo = max(st_lo, cb * SPB), cs_hi = min(st_hi, ce * SPB);
     // sub-tiles are dealt to waves round-robin by their index from st_lo
+    // three register buffers: two sub-tiles in flight while one is computed
     int st = cs_lo + ((wave - (cs_lo - st_lo) % nw) + nw) % nw;
     if (st < cs_hi) load_tile(kb0, vb0, st, cb);
+    if (st + nw < cs_hi) load_tile(kb1, vb1, st + nw, cb);
     while (st < cs_hi) {
-      const int st1 = st + nw;
-      if (st1 < cs_hi) load_tile(kb1, vb1, st1, cb);
+      if (st + 2 * nw < cs_hi) load_tile(kb2, vb2, st + 2 * nw, cb);
       compute_tile(kb0, vb0, st);
-      if (st1 >= cs_hi) break;
-      const int st2 = st1 + nw;
-      if (st2 < cs_hi) load_tile(kb0, vb0, st2, cb);
-      compute_tile(kb1, vb1, st1);
-      st = st2;
+      st += nw;
+      if (st >= cs_hi) break;
+      if (st + 2 * nw < cs_hi) load_tile(kb0, vb0, st + 2 * nw, cb);
+      compute_tile(kb1, vb1, st);
+      st += nw;
+      if (st >= cs_hi) break;
+      if (st + 2 * nw < cs_hi) load_tile(kb1, vb1, st + 2 * nw, cb);
+      compute_tile(kb2, vb2, st);
+      st += nw;
     }
   }
 

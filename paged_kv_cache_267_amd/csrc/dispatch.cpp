@@ -5,9 +5,17 @@
 
 namespace pa {
 
+// The matrix cores take groups of 8 or more query heads per KV head; smaller
+// groups use the VALU bandwidth path (f32 caches always do).
+bool decode_uses_mfma(int kv_dtype, int G) { return kv_dtype != PA_F32 && G >= 8; }
+
 hipError_t dispatch_decode(const DecodeParams& p, int kv_dtype, int D, int BS, int G, int parts,
                            hipStream_t stream) {
   const int waves = VALU_WAVES;
+  if (decode_uses_mfma(kv_dtype, G)) {
+    if (kv_dtype == PA_BF16) return decode_mfma_bf16(p, D, BS, G, parts, stream);
+    return decode_mfma_fp8(p, D, BS, G, parts, stream);
+  }
   switch (kv_dtype) {
     case PA_F32: return decode_valu_f32(p, D, BS, G, parts, waves, stream);
     case PA_BF16: return decode_valu_bf16(p, D, BS, G, parts, waves, stream);

@@ -20,6 +20,15 @@ hipError_t decode_valu_bf16(const DecodeParams& p, int D, int BS, int G, int par
 hipError_t decode_valu_fp8(const DecodeParams& p, int D, int BS, int G, int parts, int waves,
                            hipStream_t stream);
 
+// Matrix-core path (bf16 / E4M3 caches, G in {1, 2, 4, 8, 16}).
+hipError_t decode_mfma_bf16(const DecodeParams& p, int D, int BS, int G, int parts,
+                            hipStream_t stream);
+hipError_t decode_mfma_fp8(const DecodeParams& p, int D, int BS, int G, int parts,
+                           hipStream_t stream);
+
+// True when the matrix-core kernel serves (KV dtype, group size).
+bool decode_uses_mfma(int kv_dtype, int G);
+
 // Chooses the kernel family for (KV dtype, group size) and launches it with a
 // grid of (num_kv_heads, parts, num_seqs).
 hipError_t dispatch_decode(const DecodeParams& p, int kv_dtype, int D, int BS, int G, int parts,
