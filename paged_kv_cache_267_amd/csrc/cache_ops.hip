@@ -46,46 +46,85 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
 // Merge of per-partition results by their log-sum-exp: for each (sequence,
 // query head) with keys [lo, L), partitions p with [pP, (p+1)P) meeting that
 // range are combined as sum_p e^(lse_p - M) o_p / sum_p e^(lse_p - M).
-// One wave per row; lane l owns head_dim entries l, l+64.
-template <bool OUT_BF16>
-__global__ __launch_bounds__(64) void reduce_lse_kernel(
+// One 256-thread workgroup per row: the weights go to LDS, then thread t sums
+// float4 column t % (D/4) over partitions t / (D/4), t / (D/4) + SLOTS, ...
+// so 8 (D = 128) or 16 (D = 64) partitions are read at once, and the slots
+// are folded through LDS at the end.
+constexpr int RED_THREADS = 256;
+constexpr int RED_CHUNK = 1024;  // partitions whose weights are staged at a time
+
+template <bool OUT_BF16, int D>
+__global__ __launch_bounds__(RED_THREADS) void reduce_lse_kernel(
     const float* __restrict__ part_out, const float* __restrict__ part_lse,
-    const int32_t* __restrict__ seq_lens, void* __restrict__ out, int Hq, int D,
-    int partition_size, int max_parts, int window) {
-  const int hq = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+    const int32_t* __restrict__ seq_lens, void* __restrict__ out, int Hq, int partition_size,
+    int max_parts, int window) {
+  constexpr int COLS = D / 4;                 // float4 columns per partition
+  constexpr int SLOTS = RED_THREADS / COLS;   // partitions read in parallel
+  __shared__ float w_s[RED_CHUNK];
+  __shared__ float red[RED_THREADS / 64];
+  __shared__ float4 acc_s[SLOTS][COLS];
+  const int hq = blockIdx.x, s = blockIdx.y, t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
   int L = seq_lens[s];
   L = L < 0 ? 0 : L;
   const int lo = (window > 0 && L > window) ? L - window : 0;
-  int p_lo = lo / partition_size;
-  int p_hi = (L + partition_size - 1) / partition_size;
-  if (p_hi > max_parts) p_hi = max_parts;
+  const int p_lo = lo / partition_size;
+  const int p_hi = min(max_parts, (L + partition_size - 1) / partition_size);
   const size_t row = (size_t)s * Hq + hq;
+  const float* lse = part_lse + row * max_parts;
+
+  // M = max over the row's partitions
   float mx = -INFINITY;
-  for (int q = p_lo + lane; q < p_hi; q += 64) mx = fmaxf(mx, part_lse[row * max_parts + q]);
+  for (int q = p_lo + t; q < p_hi; q += RED_THREADS) mx = fmaxf(mx, lse[q]);
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  float num0 = 0.f, num1 = 0.f, den = 0.f;
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
+  const int col = t % COLS, slot = t / COLS;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
   if (L > 0 && mx != -INFINITY) {
-    for (int q = p_lo; q < p_hi; ++q) {
-      const float lse = part_lse[row * max_parts + q];
-      const float w = lse == -INFINITY ? 0.f : __expf(lse - mx);
-      const float* o = part_out + (row * max_parts + q) * D;
-      den += w;
-      if (w != 0.f) {
-        num0 += w * o[lane];
-        if (D > 64) num1 += w * o[lane + 64];
+    for (int c0 = p_lo; c0 < p_hi; c0 += RED_CHUNK) {
+      const int c1 = min(p_hi, c0 + RED_CHUNK);
+      __syncthreads();
+      for (int q = c0 + t; q < c1; q += RED_THREADS) {
+        const float l = lse[q];
+        w_s[q - c0] = l == -INFINITY ? 0.f : __expf(l - mx);
+      }
+      __syncthreads();
+      if (t < COLS)
+        for (int q = c0; q < c1; ++q) den += w_s[q - c0];
+#pragma unroll 4
+      for (int q = c0 + slot; q < c1; q += SLOTS) {
+        const float w = w_s[q - c0];
+        if (w != 0.f) {  // skipped partitions may hold anything
+          const float4 o = *(const float4*)(part_out + (row * max_parts + q) * D + 4 * col);
+          a.x += w * o.x; a.y += w * o.y; a.z += w * o.z; a.w += w * o.w;
+        }
       }
     }
-    num0 /= den;
-    num1 /= den;
   }
-  if (OUT_BF16) {
-    uint16_t* ob = (uint16_t*)out + row * D;
-    ob[lane] = to_bf16_bits(num0);
-    if (D > 64) ob[lane + 64] = to_bf16_bits(num1);
-  } else {
-    float* of = (float*)out + row * D;
-    of[lane] = num0;
-    if (D > 64) of[lane + 64] = num1;
+  acc_s[slot][col] = a;
+  __syncthreads();
+  if (t < COLS) {
+    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < SLOTS; ++k) {
+      const float4 v = acc_s[k][t];
+      r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
+    }
+    if (den > 0.f) {
+      const float inv = 1.f / den;
+      r.x *= inv; r.y *= inv; r.z *= inv; r.w *= inv;
+    }
+    if (OUT_BF16) {
+      uint2 b;
+      b.x = pack_bf16x2(r.x, r.y);
+      b.y = pack_bf16x2(r.z, r.w);
+      *(uint2*)((uint16_t*)out + row * D + 4 * t) = b;
+    } else {
+      *(float4*)((float*)out + row * D + 4 * t) = r;
+    }
   }
 }
 
@@ -128,13 +167,22 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc
 hipError_t launch_reduce_lse(const float* part_out, const float* part_lse,
                              const int32_t* seq_lens, int S, int Hq, int D, int P, int max_parts,
                              int window, void* out, bool out_bf16, hipStream_t stream) {
-  dim3 grid(Hq, S);
-  if (out_bf16)
-    hipLaunchKernelGGL(reduce_lse_kernel<true>, grid, dim3(64), 0, stream, part_out, part_lse,
-                       seq_lens, out, Hq, D, P, max_parts, window);
-  else
-    hipLaunchKernelGGL(reduce_lse_kernel<false>, grid, dim3(64), 0, stream, part_out, part_lse,
-                       seq_lens, out, Hq, D, P, max_parts, window);
+  dim3 grid(Hq, S), block(RED_THREADS);
+  if (D == 128) {
+    if (out_bf16)
+      hipLaunchKernelGGL((reduce_lse_kernel<true, 128>), grid, block, 0, stream, part_out,
+                         part_lse, seq_lens, out, Hq, P, max_parts, window);
+    else
+      hipLaunchKernelGGL((reduce_lse_kernel<false, 128>), grid, block, 0, stream, part_out,
+                         part_lse, seq_lens, out, Hq, P, max_parts, window);
+  } else {
+    if (out_bf16)
+      hipLaunchKernelGGL((reduce_lse_kernel<true, 64>), grid, block, 0, stream, part_out,
+                         part_lse, seq_lens, out, Hq, P, max_parts, window);
+    else
+      hipLaunchKernelGGL((reduce_lse_kernel<false, 64>), grid, block, 0, stream, part_out,
+                         part_lse, seq_lens, out, Hq, P, max_parts, window);
+  }
   return hipGetLastError();
 }
 
