@@ -140,7 +140,8 @@ int pa_decode(const void* query, const void* key_cache, const void* value_cache,
  *           softmax-weighted V of the partition (already divided by its sum).
  * part_lse  fp32 [num_seqs][num_q_heads][max_num_partitions]: natural-log
  *           log-sum-exp of the partition's scaled scores s_j.
- * For an empty partition part_lse is -inf and part_out is not written.
+ * Only partitions that meet [lo, L) are written; the entries of the others
+ * are left as they are (pa_reduce_lse never reads them).
  * Both buffers together are pa_decode_split_workspace_bytes(...) bytes.
  */
 int pa_decode_split(const void* query, const void* key_cache, const void* value_cache,

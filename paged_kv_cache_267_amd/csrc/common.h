@@ -39,6 +39,7 @@ struct DecodeParams {
   int max_blocks, num_blocks, window;
   int partition_size;   // tokens per partition (split); 0 = whole sequence
   int max_parts;
+  int seq_begin, seq_count;  // sequences of this launch (persistent schedule)
 };
 
 // ---- scalar conversions ------------------------------------------------------
@@ -125,5 +126,16 @@ __device__ __forceinline__ float swap_add16(float a, float b) {
 }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return uniform((int)(threadIdx.x >> 6)); }
+
+// Workgroup barrier ordering LDS only: the calling waves' outstanding global
+// loads stay in flight across it (a full __syncthreads would drain them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 }  // namespace pa

@@ -1,26 +1,47 @@
-// decode_mfma.h -- paged decode attention on the gfx950 matrix cores.
+// decode_mfma.h -- paged decode attention on the gfx950 matrix cores, with a
+// persistent, balanced schedule.
 //
-// Same computation as the bandwidth path (decode_valu.h; sources: "vLLM 0.5
-// deep dive: PagedAttention architecture", chenxutan.com, s2.2-s2.3, and
-// "vLLM 0.7.2 deep dive: PagedAttention v2 with FlashAttention-3", jsqmd.com,
-// s2.2-s2.3), with both contractions of a 16-token sub-tile on MFMA:
+// Computation (sources: "vLLM 0.5 deep dive: PagedAttention architecture",
+// chenxutan.com, s2.2-s2.3; "vLLM 0.7.2 deep dive: PagedAttention v2 with
+// FlashAttention-3", jsqmd.com, s2.2-s2.3): per (sequence, query head), scaled
+// dot products of the query with every in-window key, gathered block by block
+// through the block table, a softmax kept stable by a running max and sum, and
+// the softmax-weighted sum of the values.  Both contractions of a 16-token
+// sub-tile run on MFMA:
+//   S^T = K . Q^T     v_mfma_f32_16x16x32_bf16: A = K (16 tokens x 32 dims, the
+//                     16-byte K groups exactly as they sit in the cache),
+//                     B = Q^T (32 dims x 16 heads; heads >= G are zero);
+//   O^T += V^T . P^T  v_mfma_f32_16x16x16_bf16: A = V^T (16 dims x 16 tokens,
+//                     4 consecutive tokens of one V row per lane), B = P^T.
+// Heads sit on the N axis, so lane l owns head l%16 in every fragment: the S^T
+// C-fragment is bit for bit the P^T B-fragment, and a head's running max, sum
+// and rescale are lane-local.  Per sub-tile the only cross-lane step is the
+// column max over the 4 lane rows (two permlane swaps).  The running max is
+// updated lazily: accumulators are rescaled only when a head's max grows by
+// more than 2^8, so p <= 256.  E4M3 codes are converted to bf16 in registers
+// (exact); k_scale is folded into the score scale, v_scale applied at the end.
 //
-//   S^T = K . Q^T   v_mfma_f32_16x16x32_bf16, A = K (16 tokens x 32 dims, the
-//                   16-byte K groups exactly as they sit in the cache),
-//                   B = Q^T (32 dims x 16 heads; heads >= G are zero)
-//   O^T += V^T . P^T  v_mfma_f32_16x16x16_bf16, A = V^T (16 dims x 16 tokens:
-//                   4 consecutive tokens of one V row per lane), B = P^T.
+// Schedule.  A segment is one output unit: a partition (split) or a whole
+// sequence (unsplit).  The grid is sized to the resident capacity; workgroup w
+// serves KV head w % H_kv (workgroups are dealt to the 8 XCDs round-robin, so a
+// head stays on one XCD and a prefix shared by many sequences stays in its L2)
+// and takes that head's segments from one list, dealt to its J workgroups in
+// serpentine rounds: full partitions first (by sequence), then the partial ones
+// (a sequence's first or last partition, or the whole sequence when unsplit),
+// largest first.  Each workgroup builds the list from the lengths in LDS.
 //
-// With heads on the N axis, lane l owns head l%16 in every fragment: the C
-// fragment of S^T (tokens 4*(l/16)+j) is bit for bit the B fragment PV needs,
-// and the running max, sum and rescale of a head are lane-local.  The only
-// cross-lane step per sub-tile is the column max over the 4 lane rows (two
-// permlane swaps).  The running max is updated lazily: the accumulators are
-// rescaled only when a column's max grows by more than 2^8, so p <= 256.
-//
-// E4M3 caches: K and V codes are converted to bf16 in registers (exact) with
-// the hardware pair conversion; k_scale is folded into the score scale and
-// v_scale applied at the end.
+// Memory pipeline.  The workgroup walks its segments in batches.  For a batch
+// it stages, in LDS, the block-table entries of every block the batch touches
+// and the query rows of its segments; after that the only global loads until
+// the batch ends are K/V sub-tiles.  Each wave streams its sub-tiles (the 4
+// waves take a segment's 16-token sub-tiles round-robin) two tiles ahead
+// across segment boundaries, with a fixed number of loads per step (a wave
+// past its last tile re-reads block 0), so every wait before a tile's first
+// use leaves the two younger tiles in flight.  Segment ends merge the 4 waves'
+// (max, sum, acc) through LDS behind barriers that order LDS only, and write
+// the output (unsplit) or the partition's output and natural-log LSE (split).
+// A segment longer than the staged table is carried into the next batch with
+// its running state.
 #pragma once
 
 #include "common.h"
@@ -31,15 +52,50 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int MFMA_WAVES = 4;
-constexpr int MFMA_TBL_CAP = 512;
+constexpr int MFMA_SEQ_CHUNK = 1024;   // sequences per launch (prefix kept in LDS)
+constexpr int MFMA_TBL = 2048;         // block-table entries staged per batch
 constexpr float LAZY_RESCALE_LOG2 = 8.0f;
+// register buffers per wave: NBUF - 1 sub-tiles in flight while one is
+// computed (E4M3 sub-tiles are half the bytes, so twice as many)
+template <int KV> struct MfmaDepth { static constexpr int NBUF = KV == KV_FP8 ? 5 : 3; };
 
-template <int KV, int D, int G>
+template <int D, int G>
+struct MfmaGeom {
+  static constexpr int QROW = D + 8;                       // padded query row (elements)
+  static constexpr int QBYTES = G <= 8 ? 16384 : 8192;     // LDS for staged queries
+  static constexpr int SLOTS_RAW = QBYTES / (G * QROW * 2);
+  static constexpr int SLOTS = SLOTS_RAW < 32 ? SLOTS_RAW : 32;  // segments per batch
+};
+
+// Per-batch description of one segment slot.
+struct SegMeta {
+  int s;        // sequence (relative to the launch)
+  int p;        // partition (split) or 0
+  int t0, t1;   // key range of the whole segment
+  int st_a;     // first sub-tile of this batch's share of the segment
+  int st_b;     // end sub-tile of this batch's share
+  int tbl;      // LDS table index of block st_a / SPB
+  int fin;      // the segment ends in this batch
+};
+
+constexpr int MFMA_SORT_MAX = 512;     // partial segments ordered by size (more: by sequence)
+
+template <int D, int G>
 struct MfmaSmem {
-  int32_t table[MFMA_TBL_CAP];
+  int32_t lens[MFMA_SEQ_CHUNK];        // clamped lengths
+  int32_t fpre[MFMA_SEQ_CHUNK + 1];    // full partitions before each sequence (exclusive)
+  int32_t ppre[MFMA_SEQ_CHUNK + 1];    // partial segments before each sequence (exclusive)
+  int32_t plist[MFMA_SORT_MAX];        // partial segments, largest first: (s << 20) | p
+  int32_t tbl[MFMA_TBL];               // staged block ids of the batch
+  uint16_t q[MfmaGeom<D, G>::SLOTS][G][MfmaGeom<D, G>::QROW];
+  SegMeta meta[MfmaGeom<D, G>::SLOTS];
+  int32_t bcount, bnext_m, bnext_st, scan[2][MFMA_WAVES];
   float m[MFMA_WAVES][G];
   float l[MFMA_WAVES][G];
-  float acc[MFMA_WAVES][G][D];
+  union {
+    float acc[MFMA_WAVES][G][D + 4];   // merge area (rows padded: no bank conflicts)
+    int32_t pkey[MFMA_SORT_MAX];       // sort keys, before any merge
+  } u;
 };
 
 __device__ __forceinline__ float colmax4(float x) {
@@ -50,257 +106,513 @@ __device__ __forceinline__ float colmax4(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float colsum4(float x) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const float y = swap_add32(x, x);
+  return swap_add16(y, y);
 }
 
 template <int KV, int D, int BS, int G>
 __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodeParams p) {
   static_assert(KV == KV_BF16 || KV == KV_FP8, "matrix path takes bf16 or E4M3 caches");
   static_assert(G <= 16, "at most 16 query heads per KV head");
+  using Geo = MfmaGeom<D, G>;
   constexpr int E = KvTraits<KV>::E;
   constexpr int KS = D / 32;          // QK k-steps of 32 dims
   constexpr int NB = D / 16;          // PV n-blocks of 16 dims
   constexpr int KL = D * E / 64;      // 16-byte K loads per lane per sub-tile
-  constexpr int VW = 4 * E / 4;       // V dwords per lane per n-block (bf16: 2, fp8: 1)
+  constexpr int VW = E;               // V dwords per lane per n-block (bf16: 2, fp8: 1)
   constexpr int SPB = BS / 16;
   constexpr size_t TILE_BYTES = (size_t)D * BS * E;
+  constexpr int NTH = 64 * MFMA_WAVES;
+  constexpr int SLOTS = Geo::SLOTS;
+  static_assert(SLOTS >= 1, "query staging too small");
 
-  __shared__ MfmaSmem<KV, D, G> sm;
+  __shared__ MfmaSmem<D, G> sm;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int row = lane >> 4, col = lane & 15;
-  const int hk = blockIdx.x, part = blockIdx.y, s = blockIdx.z;
-  const int Hq = p.num_q_heads;
+  const int H = p.num_kv_heads, Hq = p.num_q_heads;
+  const int hk = blockIdx.x % H;
+  const int j = blockIdx.x / H, J = gridDim.x / H;
+  const int S = p.seq_count, s0 = p.seq_begin;
+  const int P = p.partition_size;     // 0: unsplit
+  const int Lmax = p.max_blocks * BS;
 
-  int L = p.seq_lens[s];
-  L = L < 0 ? 0 : (L > p.max_blocks * BS ? p.max_blocks * BS : L);
-  const int lo = (p.window > 0 && L > p.window) ? L - p.window : 0;
-  int t0 = lo, t1 = L;
-  if (p.partition_size > 0) {
-    t0 = max(lo, part * p.partition_size);
-    t1 = min(L, (part + 1) * p.partition_size);
-  }
-  if (t0 >= t1) {
-    if (p.part_out == nullptr) {
-      for (int i = threadIdx.x; i < G * D; i += blockDim.x)
-        ((uint16_t*)p.out)[((size_t)s * Hq + hk * G + i / D) * D + i % D] = 0;
-    } else if (threadIdx.x < G) {
-      p.part_lse[((size_t)s * Hq + hk * G + threadIdx.x) * p.max_parts + part] = -INFINITY;
-    }
-    return;
-  }
-
-  // ---- Q^T as the B operand of each QK k-step (zero for heads >= G) ----------
-  bf16x8_t qop[KS];
+  // ---- schedule: full partitions first (by sequence), then the partial ones --
+  // (first / last partition of a sequence, or the whole sequence when unsplit)
+  // largest first.
+  auto seg_range = [&](int L, int pp, int& t0, int& t1) {
+    const int lo = (p.window > 0 && L > p.window) ? L - p.window : 0;
+    if (P == 0) { t0 = lo; t1 = L; return; }
+    t0 = max(lo, pp * P);
+    t1 = min(L, (pp + 1) * P);
+  };
+  auto counts = [&](int L, int& nfull, int& npart, int& pf0) {
+    // pf0: first full partition; partial ones are p_lo and/or p_hi - 1
+    nfull = 0; npart = 0; pf0 = 0;
+    if (P == 0) { npart = 1; return; }
+    if (L <= 0) return;
+    const int lo = (p.window > 0 && L > p.window) ? L - p.window : 0;
+    const int p_lo = lo / P, p_hi = (L + P - 1) / P;
+    pf0 = (lo + P - 1) / P;
+    nfull = max(0, L / P - pf0);
+    npart = (p_hi - p_lo) - nfull;
+  };
   {
-    const uint16_t* qrow = (const uint16_t*)p.q + ((size_t)s * Hq + hk * G + col) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      // dims of k-step ks held by lane row r: bf16 -> 32ks + 8r; E4M3 -> the
-      // matching half of 16-byte group r + 4*(ks/2)
-      const int d0 = (KV == KV_BF16) ? 32 * ks + 8 * row : 16 * (row + 4 * (ks >> 1)) + 8 * (ks & 1);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (col < G) v = *(const uint4*)(qrow + d0);
-      qop[ks] = __builtin_bit_cast(bf16x8_t, (u32x4_t){v.x, v.y, v.z, v.w});
+    const int per = (S + NTH - 1) / NTH;
+    const int a = min(S, tid * per), b = min(S, a + per);
+    int cf = 0, cp = 0;
+    for (int i = a; i < b; ++i) {
+      int L = p.seq_lens[s0 + i];
+      L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+      sm.lens[i] = L;
+      int nf, np, f0;
+      counts(L, nf, np, f0);
+      cf += nf;
+      cp += np;
     }
-  }
-
-  f32x4_t acc[NB];
+    int xf = cf, xp = cp;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY, l_run = 0.f;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int yf = __shfl_up(xf, off, 64), yp = __shfl_up(xp, off, 64);
+      if (lane >= off) { xf += yf; xp += yp; }
+    }
+    if (lane == 63) { sm.scan[0][wave] = xf; sm.scan[1][wave] = xp; }
+    __syncthreads();
+    int rf = xf - cf, rp = xp - cp;
+    for (int w = 0; w < wave; ++w) { rf += sm.scan[0][w]; rp += sm.scan[1][w]; }
+    for (int i = a; i < b; ++i) {
+      sm.fpre[i] = rf;
+      sm.ppre[i] = rp;
+      int nf, np, f0;
+      counts(sm.lens[i], nf, np, f0);
+      rf += nf;
+      rp += np;
+    }
+    if (tid == NTH - 1) { sm.fpre[S] = rf; sm.ppre[S] = rp; }
+    __syncthreads();
+  }
+  const int F = uniform(sm.fpre[S]), NPART = uniform(sm.ppre[S]);
+  const bool sorted = NPART <= MFMA_SORT_MAX;
+  if (sorted) {
+    // list the partial segments with their sizes, then place each by its rank
+    // under (size desc, sequence asc, partition asc)
+    for (int i = tid; i < S; i += NTH) {
+      const int L = sm.lens[i];
+      int nf, np, f0;
+      counts(L, nf, np, f0);
+      int o = sm.ppre[i];
+      if (np > 0) {
+        const int lo = (p.window > 0 && L > p.window) ? L - p.window : 0;
+        const int p_lo = P ? lo / P : 0, p_hi = P ? (L + P - 1) / P : 1;
+        for (int pp = p_lo; pp < p_hi; pp = (pp == p_lo && p_hi - 1 > p_lo) ? p_hi - 1 : p_hi) {
+          int t0, t1;
+          seg_range(L, pp, t0, t1);
+          if (P != 0 && t1 - t0 == P) continue;
+          sm.plist[o] = (i << 20) | pp;
+          sm.u.pkey[o] = t1 - t0;
+          ++o;
+        }
+      }
+    }
+    __syncthreads();
+    int mine[MFMA_SORT_MAX / NTH], rk[MFMA_SORT_MAX / NTH], ky[MFMA_SORT_MAX / NTH];
+#pragma unroll
+    for (int r = 0; r < MFMA_SORT_MAX / NTH; ++r) {
+      const int e = tid + r * NTH;
+      mine[r] = e < NPART ? sm.plist[e] : 0;
+      ky[r] = e < NPART ? sm.u.pkey[e] : 0;
+      rk[r] = 0;
+    }
+    for (int f = 0; f < NPART; ++f) {
+      const int kf = sm.u.pkey[f], vf = sm.plist[f];
+#pragma unroll
+      for (int r = 0; r < MFMA_SORT_MAX / NTH; ++r)
+        rk[r] += (kf > ky[r] || (kf == ky[r] && vf < mine[r])) ? 1 : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < MFMA_SORT_MAX / NTH; ++r)
+      if (tid + r * NTH < NPART) sm.plist[rk[r]] = mine[r];
+    __syncthreads();
+  }
+  const int total = F + NPART;
+  // workgroup j takes list entries in serpentine order: round r gives it entry
+  // r*J + j (r even) or r*J + J-1-j (r odd), so the largest entries of one
+  // round meet the smallest of the next
+  auto list_index = [&](int m) -> int { return m * J + ((m & 1) ? J - 1 - j : j); };
+  int M = total / J;  // full rounds, then possibly one entry of the last round
+  if (M * J < total && list_index(M) < total) ++M;
+
+  // k-th segment of the list -> (sequence, partition)
+  auto seg_of = [&](int k, int& si, int& pp) {
+    const bool full = k < F;
+    const int kk = full ? k : k - F;
+    if (!full && sorted) {
+      const int e = uniform(sm.plist[kk]);
+      si = e >> 20;
+      pp = e & 0xfffff;
+      return;
+    }
+    const int32_t* pre = full ? sm.fpre : sm.ppre;
+    si = 0;
+    for (;;) {
+      const int i = si + lane;
+      const int v = i < S ? pre[i + 1] : 0x7fffffff;
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(v > kk);
+      if (hit) { si += __builtin_ctzll(hit); break; }
+      si += 64;
+    }
+    const int L = uniform(sm.lens[si]);
+    int nf, np, f0;
+    counts(L, nf, np, f0);
+    const int r = kk - uniform(pre[si]);
+    if (full) {
+      pp = f0 + r;
+    } else {
+      const int lo = (p.window > 0 && L > p.window) ? L - p.window : 0;
+      const int p_lo = P ? lo / P : 0, p_hi = P ? (L + P - 1) / P : 1;
+      int t0, t1;
+      seg_range(L, p_lo, t0, t1);
+      const bool first_partial = P == 0 || t1 - t0 != P;
+      pp = (r == 0 && first_partial) ? p_lo : p_hi - 1;
+    }
+  };
 
   const char* kbase = (const char*)p.kc + (size_t)hk * TILE_BYTES;
   const char* vbase = (const char*)p.vc + (size_t)hk * TILE_BYTES;
-  const size_t block_stride = (size_t)p.num_kv_heads * TILE_BYTES;
-  const int32_t* table_row = p.block_tables + (size_t)s * p.max_blocks;
+  const size_t block_stride = (size_t)H * TILE_BYTES;
   const unsigned nb_max = (unsigned)(p.num_blocks - 1);
 
-  uint32_t koff[KL];
-#pragma unroll
-  for (int i = 0; i < KL; ++i) koff[i] = (uint32_t)(((row + 4 * i) * BS + col) * 16);
-  // V: row d = 16*nb + col, tokens 4*row .. 4*row+3 of the sub-tile
+  // lane offsets inside a sub-tile
+  const uint32_t koff0 = (uint32_t)((row * BS + col) * 16);
   const uint32_t voff0 = (uint32_t)((col * BS + 4 * row) * E);
-
-  const int st_lo = t0 >> 4, st_hi = (t1 + 15) >> 4;
-  const int b_lo = st_lo / SPB, b_hi = (st_hi + SPB - 1) / SPB;
 
   struct Buf {
     uint4 k[KL];
     uint32_t v[NB][VW];
+    int slot;   // segment slot in the batch (-1: no tile)
+    int st;     // sub-tile index
   };
-  Buf buf0, buf1, buf2;
+  Buf bufs[MfmaDepth<KV>::NBUF];
 
-  auto load_tile = [&](Buf& b, int st, int tbl_base) {
-    const int phys = uniform(sm.table[st / SPB - tbl_base]);
-    const int sub = st % SPB;
-    const char* kp = kbase + (size_t)phys * block_stride + sub * 256;
-    const char* vp = vbase + (size_t)phys * block_stride + sub * 16 * E + voff0;
+  // running state of the segment being computed (carried across batches when a
+  // segment continues)
+  f32x4_t acc[NB];
+  float m_ref = -INFINITY, l_run = 0.f;
 #pragma unroll
-    for (int i = 0; i < KL; ++i) b.k[i] = load_nt16(kp + koff[i]);
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  bf16x8_t qop[KS];
+
+  auto reset = [&]() {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const char* a = vp + (size_t)nb * 16 * BS * E;
-      if (VW == 2) {
-        const u32x2_t t = __builtin_nontemporal_load((const u32x2_t*)a);
-        b.v[nb][0] = t.x;
-        b.v[nb][VW - 1] = t.y;
-      } else {
-        b.v[nb][0] = __builtin_nontemporal_load((const uint32_t*)a);
-      }
-    }
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    m_ref = -INFINITY;
+    l_run = 0.f;
   };
 
-  auto compute_tile = [&](Buf& b, int st) {
-    // S^T for this sub-tile
-    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < KL; ++i) {
-      if (KV == KV_BF16) {
-        const bf16x8_t kop = __builtin_bit_cast(bf16x8_t, (u32x4_t){b.k[i].x, b.k[i].y, b.k[i].z, b.k[i].w});
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[i], sacc, 0, 0, 0);
-      } else {
-        const u32x4_t lo4 = {fp8x2_to_bf16x2<false>(b.k[i].x), fp8x2_to_bf16x2<true>(b.k[i].x),
-                             fp8x2_to_bf16x2<false>(b.k[i].y), fp8x2_to_bf16x2<true>(b.k[i].y)};
-        const u32x4_t hi4 = {fp8x2_to_bf16x2<false>(b.k[i].z), fp8x2_to_bf16x2<true>(b.k[i].z),
-                             fp8x2_to_bf16x2<false>(b.k[i].w), fp8x2_to_bf16x2<true>(b.k[i].w)};
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo4),
-                                                       qop[2 * i], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi4),
-                                                       qop[2 * i + 1], sacc, 0, 0, 0);
+  int bm = 0, bst = -1;  // next batch starts at segment bm, sub-tile bst (-1: its start)
+
+  while (bm < M) {
+    // ---- batch plan (wave 0, scalar) -----------------------------------------------
+    if (wave == 0) {
+      int m = bm, st_start = bst, cnt = 0, used = 0;
+      int next_m = M, next_st = -1;
+      while (m < M && cnt < SLOTS) {
+        int si, pp;
+        seg_of(list_index(m), si, pp);
+        const int L = uniform(sm.lens[si]);
+        int t0, t1;
+        seg_range(L, pp, t0, t1);
+        const int st_lo = t0 >> 4, st_hi = t0 < t1 ? (t1 + 15) >> 4 : st_lo;
+        const int a = st_start >= 0 ? st_start : st_lo;
+        // this batch's share of the segment: sub-tiles [a, b), blocks
+        // [a / SPB, ceil(b / SPB)); a segment that does not fit starts a new batch,
+        // unless it is the first slot (then it takes what fits and continues)
+        int b = st_hi;
+        const int room = MFMA_TBL - used;
+        if (b > a && (b + SPB - 1) / SPB - a / SPB > room) {
+          if (cnt > 0) { next_m = m; next_st = st_start; break; }
+          b = (a / SPB + room) * SPB;
+        }
+        const int nblk = b > a ? (b + SPB - 1) / SPB - a / SPB : 0;
+        if (lane == 0) {
+          SegMeta& md = sm.meta[cnt];
+          md.s = si; md.p = pp; md.t0 = t0; md.t1 = t1;
+          md.st_a = a; md.st_b = b; md.tbl = used; md.fin = b >= st_hi ? 1 : 0;
+        }
+        used += nblk;
+        ++cnt;
+        if (b < st_hi) { next_m = m; next_st = b; break; }
+        ++m;
+        st_start = -1;
+        next_m = m;
+        next_st = -1;
+      }
+      if (lane == 0) {
+        sm.bcount = cnt;
+        sm.bnext_m = next_m;
+        sm.bnext_st = next_st;
       }
     }
-    float sc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sc[j] = sacc[j] * p.qk_scale;
+    __syncthreads();
+    const int nslot = uniform(sm.bcount);
+    bm = uniform(sm.bnext_m);
+    bst = uniform(sm.bnext_st);
 
-    const bool partial = (st * 16 < t0) || (st * 16 + 16 > t1);
-    if (partial) {
-      uint32_t vmask[VW];
+    // ---- stage block ids and queries of the batch ------------------------------------
+    for (int c = 0; c < nslot; ++c) {
+      const int si = uniform(sm.meta[c].s), a = uniform(sm.meta[c].st_a);
+      const int b = uniform(sm.meta[c].st_b), t = uniform(sm.meta[c].tbl);
+      const int blk0 = a / SPB, nblk = b > a ? (b + SPB - 1) / SPB - blk0 : 0;
+      const int32_t* trow = p.block_tables + (size_t)(s0 + si) * p.max_blocks + blk0;
+      for (int i = tid; i < nblk; i += NTH) {
+        const unsigned id = (unsigned)trow[i];
+        sm.tbl[t + i] = (int)(id > nb_max ? nb_max : id);
+      }
+      const uint16_t* qsrc = (const uint16_t*)p.q + ((size_t)(s0 + si) * Hq + hk * G) * D;
+      for (int i = tid; i < G * D / 8; i += NTH)
+        *(uint4*)&sm.q[c][(i * 8) / D][(i * 8) % D] = *(const uint4*)(qsrc + i * 8);
+    }
+    __syncthreads();
+
+    // ---- tile stream of this wave over the batch's slots -------------------------------
+    // Sub-tiles are dealt to the waves round-robin from the segment's first
+    // sub-tile; first_st(c) is this wave's first sub-tile >= st_a in slot c.
+    auto first_st = [&](int c) -> int {
+      const int st_lo = uniform(sm.meta[c].t0) >> 4, a = uniform(sm.meta[c].st_a);
+      return a + (((wave - (a - st_lo)) % MFMA_WAVES) + MFMA_WAVES) % MFMA_WAVES;
+    };
+    auto next_st = [&](int st) -> int { return st + MFMA_WAVES; };
+    int cs = 0, cst = nslot > 0 ? first_st(0) : 0;   // load cursor: slot, sub-tile
+    auto settle = [&]() {        // move the cursor to a slot with a tile left
+      while (cs < nslot && cst >= uniform(sm.meta[cs].st_b)) {
+        ++cs;
+        if (cs < nslot) cst = first_st(cs);
+      }
+    };
+    settle();
+
+    auto load_tile = [&](Buf& b) {
+      int phys = 0, st = 0;
+      if (cs < nslot) {
+        st = cst;
+        const int blk = st / SPB - uniform(sm.meta[cs].st_a) / SPB;
+        phys = uniform(sm.tbl[uniform(sm.meta[cs].tbl) + blk]);
+        b.slot = cs;
+        b.st = st;
+        cst = next_st(cst);
+        settle();
+      } else {
+        b.slot = -1;             // past the end: re-read block 0 (keeps the load count fixed)
+        b.st = 0;
+      }
+      const int sub = st % SPB;
+      const char* kp = kbase + (size_t)phys * block_stride + sub * 256 + koff0;
+      const char* vp = vbase + (size_t)phys * block_stride + sub * 16 * E + voff0;
 #pragma unroll
-      for (int w = 0; w < VW; ++w) vmask[w] = 0u;
+      for (int i = 0; i < KL; ++i) b.k[i] = load_nt16(kp + i * 4 * BS * 16);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tok = st * 16 + 4 * row + j;
-        const bool ok = tok >= t0 && tok < t1;
-        if (!ok) sc[j] = -INFINITY;
-        if (ok) {
-          if (KV == KV_BF16) vmask[j >> 1] |= 0xffffu << (16 * (j & 1));
-          else vmask[0] |= 0xffu << (8 * j);
+      for (int nb = 0; nb < NB; ++nb) {
+        const char* a = vp + (size_t)nb * 16 * BS * E;
+        // a 32-token block's V row is shared by its two sub-tiles, which run on
+        // different waves: ordinary loads keep the line in L2 for the other
+        // half; 16-token rows are used whole and stream past L2
+        if (VW == 2) {
+          const u32x2_t t = SPB == 1 ? __builtin_nontemporal_load((const u32x2_t*)a)
+                                     : *(const u32x2_t*)a;
+          b.v[nb][0] = t.x;
+          b.v[nb][VW - 1] = t.y;
+        } else {
+          b.v[nb][0] = SPB == 1 ? __builtin_nontemporal_load((const uint32_t*)a)
+                                : *(const uint32_t*)a;
         }
       }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int w = 0; w < VW; ++w) b.v[nb][w] &= vmask[w];
-    }
+    };
 
-    // column max, lazy rescale, probabilities
-    const float cmax = colmax4(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-    const bool grow = cmax > m_ref + LAZY_RESCALE_LOG2;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = fmaxf(m_ref, cmax);
-      const float alpha = fast_exp2(m_ref - m_new);
-      l_run *= alpha;
+    auto q_to_regs = [&](int c) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
-      m_ref = m_new;
-    }
-    float pr[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(sc[j] - m_ref);
-    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
-    const s16x4_t pop = __builtin_bit_cast(s16x4_t, (u32x2_t){p01, p23});
-
-    // O^T += V^T . P^T
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      u32x2_t vv;
-      if (KV == KV_BF16) {
-        vv = (u32x2_t){b.v[nb][0], b.v[nb][VW - 1]};
-      } else {
-        vv = (u32x2_t){fp8x2_to_bf16x2<false>(b.v[nb][0]), fp8x2_to_bf16x2<true>(b.v[nb][0])};
+      for (int ks = 0; ks < KS; ++ks) {
+        const int d0 = (KV == KV_BF16) ? 32 * ks + 8 * row : 16 * (row + 4 * (ks >> 1)) + 8 * (ks & 1);
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (col < G) v = *(const uint4*)&sm.q[c][col][d0];
+        qop[ks] = __builtin_bit_cast(bf16x8_t, (u32x4_t){v.x, v.y, v.z, v.w});
       }
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, vv), pop,
-                                                         acc[nb], 0, 0, 0);
-    }
-  };
+    };
 
-  for (int cb = b_lo; cb < b_hi; cb += MFMA_TBL_CAP) {
-    const int ce = min(b_hi, cb + MFMA_TBL_CAP);
-    __syncthreads();
-    for (int i = threadIdx.x; i < ce - cb; i += blockDim.x) {
-      const unsigned id = (unsigned)table_row[cb + i];
-      sm.table[i] = (int)(id > nb_max ? nb_max : id);
-    }
-    __syncthreads();
-    const int cs_lo = max(st_lo, cb * SPB), cs_hi = min(st_hi, ce * SPB);
-    int st = cs_lo + ((wave - (cs_lo - st_lo) % nw) + nw) % nw;
-    if (st < cs_hi) load_tile(buf0, st, cb);
-    if (st + nw < cs_hi) load_tile(buf1, st + nw, cb);
-    while (st < cs_hi) {
-      if (st + 2 * nw < cs_hi) load_tile(buf2, st + 2 * nw, cb);
-      compute_tile(buf0, st);
-      st += nw;
-      if (st >= cs_hi) break;
-      if (st + 2 * nw < cs_hi) load_tile(buf0, st + 2 * nw, cb);
-      compute_tile(buf1, st);
-      st += nw;
-      if (st >= cs_hi) break;
-      if (st + 2 * nw < cs_hi) load_tile(buf1, st + 2 * nw, cb);
-      compute_tile(buf2, st);
-      st += nw;
-    }
-  }
-
-  // ---- wave results -> LDS, merge, write ---------------------------------------
-  const float l_col = colsum4(l_run);
-  if (col < G) {
-    if (row == 0) {
-      sm.m[wave][col] = m_ref;
-      sm.l[wave][col] = l_col;
-    }
+    auto compute_tile = [&](Buf& b) {
+      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+      for (int i = 0; i < KL; ++i) {
+        if (KV == KV_BF16) {
+          const bf16x8_t kop =
+              __builtin_bit_cast(bf16x8_t, (u32x4_t){b.k[i].x, b.k[i].y, b.k[i].z, b.k[i].w});
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[i], sacc, 0, 0, 0);
+        } else {
+          const u32x4_t lo4 = {fp8x2_to_bf16x2<false>(b.k[i].x), fp8x2_to_bf16x2<true>(b.k[i].x),
+                               fp8x2_to_bf16x2<false>(b.k[i].y), fp8x2_to_bf16x2<true>(b.k[i].y)};
+          const u32x4_t hi4 = {fp8x2_to_bf16x2<false>(b.k[i].z), fp8x2_to_bf16x2<true>(b.k[i].z),
+                               fp8x2_to_bf16x2<false>(b.k[i].w), fp8x2_to_bf16x2<true>(b.k[i].w)};
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo4),
+                                                         qop[2 * i], sacc, 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi4),
+                                                         qop[2 * i + 1], sacc, 0, 0, 0);
+        }
+      }
+      float sc[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm.acc[wave][col][16 * nb + 4 * row + i] = acc[nb][i];
-  }
-  __syncthreads();
+      for (int jj = 0; jj < 4; ++jj) sc[jj] = sacc[jj] * p.qk_scale;
 
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-    const int g = i / D, d = i % D;
-    float mx = -INFINITY;
-    for (int w = 0; w < nw; ++w) mx = fmaxf(mx, sm.m[w][g]);
-    float den = 0.f, num = 0.f;
-    for (int w = 0; w < nw; ++w) {
-      const float f = sm.m[w][g] == -INFINITY ? 0.f : fast_exp2(sm.m[w][g] - mx);
-      den += f * sm.l[w][g];
-      num += f * sm.acc[w][g][d];
+      const int st = b.st;
+      const int t0 = uniform(sm.meta[b.slot].t0), t1 = uniform(sm.meta[b.slot].t1);
+      if ((st * 16 < t0) || (st * 16 + 16 > t1)) {  // partial sub-tile: mask scores, zero V
+        uint32_t vmask[VW];
+#pragma unroll
+        for (int w = 0; w < VW; ++w) vmask[w] = 0u;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int tok = st * 16 + 4 * row + jj;
+          const bool ok = tok >= t0 && tok < t1;
+          if (!ok) sc[jj] = -INFINITY;
+          if (ok) {
+            if (KV == KV_BF16) vmask[jj >> 1] |= 0xffffu << (16 * (jj & 1));
+            else vmask[0] |= 0xffu << (8 * jj);
+          }
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int w = 0; w < VW; ++w) b.v[nb][w] &= vmask[w];
+      }
+
+      const float cmax = colmax4(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+      if (__builtin_amdgcn_ballot_w64(cmax > m_ref + LAZY_RESCALE_LOG2) != 0) {
+        const float m_new = fmaxf(m_ref, cmax);
+        const float alpha = fast_exp2(m_ref - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
+        m_ref = m_new;
+      }
+      float pr[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) pr[jj] = fast_exp2(sc[jj] - m_ref);
+      l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      const s16x4_t pop = __builtin_bit_cast(
+          s16x4_t, (u32x2_t){pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        u32x2_t vv;
+        if (KV == KV_BF16) vv = (u32x2_t){b.v[nb][0], b.v[nb][VW - 1]};
+        else vv = (u32x2_t){fp8x2_to_bf16x2<false>(b.v[nb][0]), fp8x2_to_bf16x2<true>(b.v[nb][0])};
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, vv), pop,
+                                                           acc[nb], 0, 0, 0);
+      }
+    };
+
+    // ---- segment ends: merge the 4 waves and write (only slots with fin = 1) ------------
+    auto finish_slot = [&](int c) {
+      if (!uniform(sm.meta[c].fin)) return;  // continues in the next batch
+      const float l_col = colsum4(l_run);
+      if (col < G) {
+        if (row == 0) {
+          sm.m[wave][col] = m_ref;
+          sm.l[wave][col] = l_col;
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          *(f32x4_t*)&sm.u.acc[wave][col][16 * nb + 4 * row] = acc[nb];
+      }
+      lds_barrier();
+      const int s = s0 + uniform(sm.meta[c].s), pp = uniform(sm.meta[c].p);
+      for (int i = tid; i < G * D; i += NTH) {
+        const int g = i / D, d = i % D;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < MFMA_WAVES; ++w) mx = fmaxf(mx, sm.m[w][g]);
+        float den = 0.f, num = 0.f;
+        if (mx != -INFINITY) {
+#pragma unroll
+          for (int w = 0; w < MFMA_WAVES; ++w) {
+            const float f = sm.m[w][g] == -INFINITY ? 0.f : fast_exp2(sm.m[w][g] - mx);
+            den += f * sm.l[w][g];
+            num += f * sm.u.acc[w][g][d];
+          }
+        }
+        const float o = den > 0.f ? num / den * p.v_scale : 0.f;
+        const int hq = hk * G + g;
+        if (p.part_out == nullptr) {
+          ((uint16_t*)p.out)[((size_t)s * Hq + hq) * D + d] = to_bf16_bits(o);
+        } else {
+          const size_t pi = ((size_t)s * Hq + hq) * p.max_parts + pp;
+          p.part_out[pi * D + d] = o;
+          if (d == 0) p.part_lse[pi] = (mx + __log2f(den)) * 0.69314718055994531f;
+        }
+      }
+      lds_barrier();
+      reset();
+    };
+
+    // ---- main loop: NBUF buffers, NBUF - 1 tiles in flight --------------------------------
+    constexpr int NBUF = MfmaDepth<KV>::NBUF;
+    int cur = 0;                 // slot whose state the wave holds
+    q_to_regs(0);
+#pragma unroll
+    for (int i = 0; i + 1 < NBUF; ++i) load_tile(bufs[i]);
+    auto step = [&](Buf& cb, Buf& spare) -> bool {
+      load_tile(spare);
+      const int target = cb.slot < 0 ? nslot : cb.slot;
+      while (cur < target) {     // every slot is visited, in order, by every wave
+        finish_slot(cur);
+        ++cur;
+        if (cur < nslot) q_to_regs(cur);
+      }
+      if (cb.slot < 0) return false;
+      compute_tile(cb);
+      return true;
+    };
+    // the loop is left only through the exits, so every trip through the body
+    // issues the same loads and each wait leaves NBUF - 1 tiles in flight
+    for (;;) {
+#pragma unroll
+      for (int i = 0; i < NBUF; ++i)
+        if (!step(bufs[i], bufs[(i + NBUF - 1) % NBUF])) goto stream_done;
     }
-    const float o = num / den * p.v_scale;
-    const int hq = hk * G + g;
-    if (p.part_out == nullptr) {
-      ((uint16_t*)p.out)[((size_t)s * Hq + hq) * D + d] = to_bf16_bits(o);
-    } else {
-      const size_t pi = ((size_t)s * Hq + hq) * p.max_parts + part;
-      p.part_out[pi * D + d] = o;
-      if (d == 0) p.part_lse[pi] = (mx + __log2f(den)) * 0.69314718055994531f;
-    }
+  stream_done:
+    __syncthreads();           // the next batch plan overwrites the staged tables
   }
 }
 
+// Grid: resident capacity, a multiple of num_kv_heads.
 template <int KV, int D, int BS, int G>
-hipError_t launch_decode_mfma(const DecodeParams& p, int parts, hipStream_t stream) {
-  dim3 grid(p.num_kv_heads, parts, p.num_seqs);
-  hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, G>), grid, dim3(64 * MFMA_WAVES), 0, stream,
-                     p);
-  return hipGetLastError();
+hipError_t launch_decode_mfma(const DecodeParams& p0, int parts, hipStream_t stream) {
+  (void)parts;
+  static int per_cu = -1;
+  if (per_cu < 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<KV, D, BS, G>,
+                                                     64 * MFMA_WAVES, 0) != hipSuccess || n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const int H = p0.num_kv_heads;
+  DecodeParams p = p0;
+  for (int s0 = 0; s0 < p0.num_seqs; s0 += MFMA_SEQ_CHUNK) {
+    p.seq_begin = s0;
+    p.seq_count = min(MFMA_SEQ_CHUNK, p0.num_seqs - s0);
+    const long long work = (long long)p.seq_count * (p.partition_size > 0 ? p.max_parts : 1);
+    long long J = ((long long)cus * per_cu + H - 1) / H;
+    if (J > work) J = work;
+    if (J < 1) J = 1;
+    hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, G>), dim3((unsigned)(J * H)),
+                       dim3(64 * MFMA_WAVES), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace pa

@@ -85,8 +85,8 @@ __global__ __launch_bounds__(64 * VALU_MAX_WAVES) void decode_valu_kernel(Decode
   __shared__ ValuSmem<KV, D, BS, G> sm;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
+  const int wave = wave_id();
+  const int nw = uniform((int)(blockDim.x >> 6));
   const int row = lane >> 4, col = lane & 15;
   const int hk = blockIdx.x, part = blockIdx.y, s = blockIdx.z;
   const int Hq = p.num_q_heads;
@@ -343,12 +343,12 @@ __global__ __launch_bounds__(64 * VALU_MAX_WAVES) void decode_valu_kernel(Decode
   // ---- main loop over table chunks staged in LDS ------------------------------
   for (int cb = b_lo; cb < b_hi; cb += TBL_CAP) {
     const int ce = min(b_hi, cb + TBL_CAP);
-    __syncthreads();
+    lds_barrier();
     for (int i = threadIdx.x; i < ce - cb; i += blockDim.x) {
       const unsigned id = (unsigned)table_row[cb + i];
       sm.table[i] = (int)(id > nb_max ? nb_max : id);
     }
-    __syncthreads();
+    lds_barrier();
     const int cs_lo = max(st_lo, cb * SPB), cs_hi = min(st_hi, ce * SPB);
     // sub-tiles are dealt to waves round-robin by their index from st_lo
     // three register buffers: two sub-tiles in flight while one is computed
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(64 * VALU_MAX_WAVES) void decode_valu_kernel(Decode
       if (E >= 4) a += dpp<DPP_XOR2>(a);
       if (vpart == 0) sm.acc[wave][g][(lane + 64 * k) / E] = a;
     }
-  __syncthreads();
+  lds_barrier();
 
   // ---- merge waves and write ------------------------------------------------------
   for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
