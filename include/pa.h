@@ -24,7 +24,8 @@
  *
  * Conventions shared by every entry point
  *   - All buffer pointers are DEVICE pointers owned by the caller.  The
- *     library allocates nothing, keeps no state and is reentrant.
+ *     library allocates nothing and is reentrant; its only state is the
+ *     process-wide decode kernel choice (pa_set_decode_kernel).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Every call validates its arguments on the host, enqueues its kernels on
  *     `stream` and returns without synchronising.  Validation happens before
@@ -177,6 +178,44 @@ size_t pa_decode_split_workspace_bytes(int num_seqs, int num_q_heads, int head_d
  */
 int pa_fp8_e4m3_dequantize(const uint8_t* codes, float scale, float* out, long long n,
                            void* stream);
+
+/*
+ * Decode kernel family.  Two kernels compute the same operation: a vector-ALU
+ * kernel (dot products on the VALU, one workgroup per (KV head, partition,
+ * sequence)) and a matrix-core kernel (both contractions on MFMA, persistent
+ * balanced schedule; bf16 and E4M3 caches only).  PA_KERNEL_AUTO picks per
+ * call from the KV dtype and the group size G = num_q_heads / num_kv_heads;
+ * the other values force a family wherever it applies (f32 caches always run
+ * the vector-ALU kernel, groups of 16 always the matrix-core kernel).  The choice is process-wide, for tests and tuning;
+ * set it before launching work, it is not ordered against calls in flight on
+ * other host threads.
+ */
+typedef enum { PA_KERNEL_AUTO = 0, PA_KERNEL_VALU = 1, PA_KERNEL_MFMA = 2 } pa_kernel_choice;
+
+/* Sets the process-wide choice; PA_ERR_UNSUPPORTED for a value outside the enum. */
+int pa_set_decode_kernel(int choice);
+
+/* The current process-wide choice. */
+int pa_get_decode_kernel(void);
+
+/* Name of the kernel family ("valu" or "mfma") that pa_decode / pa_decode_split
+   run for these arguments under the current choice; "" if the combination is
+   not supported. */
+const char* pa_decode_kernel_name(int kv_dtype, int num_q_heads, int num_kv_heads);
+
+/*
+ * pa_probe_gather_read -- a measurement aid, not part of the attention path:
+ * reads num_chunks chunks of chunk_bytes bytes, chunk k at
+ * base + ids[k] * chunk_bytes, with the 16-byte non-temporal loads the decode
+ * kernels use for K/V tiles, and XORs all the data into *sink (one device
+ * word, not cleared).  With ids a random permutation it measures how fast HBM
+ * serves a paged gather of tiles of that size; with ids in order, a streaming
+ * read.  chunk_bytes: a power of two in [1024, 1 << 20]; base 16-byte aligned;
+ * every ids[k] must address a chunk inside the caller's buffer (not checked).
+ * grid = 0 picks 8 workgroups per compute unit.  num_chunks = 0 is a no-op.
+ */
+int pa_probe_gather_read(const void* base, const int32_t* ids, long long num_chunks,
+                         int chunk_bytes, unsigned* sink, int grid, void* stream);
 
 /* Human-readable name of a pa_status. */
 const char* pa_status_string(int status);

@@ -21,7 +21,9 @@ STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE",
 # exported symbols (include/pa.h)
 EXPORTS = ("pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_reduce_lse",
            "pa_decode_split_workspace_bytes", "pa_fp8_e4m3_dequantize", "pa_status_string",
-           "pa_last_hip_error")
+           "pa_last_hip_error", "pa_set_decode_kernel", "pa_get_decode_kernel",
+           "pa_decode_kernel_name", "pa_probe_gather_read")
+KERNEL_CHOICES = {"auto": 0, "valu": 1, "mfma": 2}
 
 
 class PaLibraryMissing(ImportError):
@@ -45,6 +47,10 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise PaLibraryMissing(
             f"{LIB_PATH} is not built; run `python -m paged_kv_cache_267_amd.build`")
+    # torch ships its own HIP runtime under the same soname as the system one;
+    # loading torch first makes libpa.so bind to that single runtime (loaded the
+    # other way round, torch would find no device)
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     L.pa_reshape_and_cache.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
@@ -59,7 +65,12 @@ def lib() -> ctypes.CDLL:
     L.pa_status_string.restype = ctypes.c_char_p
     L.pa_last_hip_error.argtypes = []
     L.pa_last_hip_error.restype = ctypes.c_char_p
-    for name in ("pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_reduce_lse",
+    L.pa_probe_gather_read.argtypes = [P, P, ctypes.c_longlong, I, P, I, P]
+    L.pa_set_decode_kernel.argtypes = [I]
+    L.pa_get_decode_kernel.argtypes = []
+    L.pa_decode_kernel_name.argtypes = [I, I, I]
+    L.pa_decode_kernel_name.restype = ctypes.c_char_p
+    for name in ("pa_probe_gather_read", "pa_set_decode_kernel", "pa_get_decode_kernel", "pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_reduce_lse",
                  "pa_fp8_e4m3_dequantize"):
         getattr(L, name).restype = I
     _lib = L
@@ -157,6 +168,46 @@ def pa_fp8_e4m3_dequantize(codes, scale, out, stream=None) -> None:
     """out[i] = value(codes[i]) * scale with the kernels' device conversion."""
     _check(lib().pa_fp8_e4m3_dequantize(_ptr(codes), float(scale), _ptr(out), codes.numel(),
                                         _stream(stream)))
+
+
+def pa_probe_gather_read(base, ids, chunk_bytes, sink, grid=0, stream=None) -> None:
+    """Bandwidth probe: read chunks base[ids[k] * chunk_bytes ...] (see pa.h)."""
+    _check(lib().pa_probe_gather_read(_ptr(base), _ptr(ids), ids.numel(), int(chunk_bytes),
+                                      _ptr(sink), int(grid), _stream(stream)))
+
+
+def pa_set_decode_kernel(choice) -> None:
+    """Process-wide decode kernel family: "auto", "valu" or "mfma" (or its code)."""
+    code = KERNEL_CHOICES[choice] if isinstance(choice, str) else int(choice)
+    _check(lib().pa_set_decode_kernel(code))
+
+
+def pa_get_decode_kernel() -> str:
+    code = lib().pa_get_decode_kernel()
+    return {v: k for k, v in KERNEL_CHOICES.items()}[code]
+
+
+def pa_decode_kernel_name(kv_dtype: int, num_q_heads: int, num_kv_heads: int) -> str:
+    """"valu" or "mfma": the family a decode call with these arguments runs ("" if
+    the combination is unsupported)."""
+    return lib().pa_decode_kernel_name(int(kv_dtype), int(num_q_heads), int(num_kv_heads)).decode()
+
+
+class decode_kernel:
+    """Context manager that sets the decode kernel family and restores the
+    previous one on exit."""
+
+    def __init__(self, choice):
+        self.choice = choice
+
+    def __enter__(self):
+        self.prev = pa_get_decode_kernel()
+        pa_set_decode_kernel(self.choice)
+        return self
+
+    def __exit__(self, *exc):
+        pa_set_decode_kernel(self.prev)
+        return False
 
 
 def decode(query, key_cache, value_cache, block_tables, seq_lens, *, block_size, scale,

@@ -191,13 +191,46 @@ int pa_fp8_e4m3_dequantize(const uint8_t* codes, float scale, float* out, long l
   return hip_status(pa::launch_fp8_dequant(codes, scale, out, n, (hipStream_t)stream));
 }
 
+int pa_probe_gather_read(const void* base, const int32_t* ids, long long num_chunks,
+                         int chunk_bytes, unsigned* sink, int grid, void* stream) {
+  if (num_chunks < 0 || grid < 0) return PA_ERR_SHAPE;
+  if (chunk_bytes < 1024 || chunk_bytes > (1 << 20) || (chunk_bytes & (chunk_bytes - 1)))
+    return PA_ERR_SHAPE;
+  if (num_chunks == 0) return PA_OK;
+  if (!base || !ids || !sink) return PA_ERR_NULL;
+  if (!aligned16(base)) return PA_ERR_ALIGN;
+  if (grid == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
+    grid = 8 * cus;
+  }
+  return hip_status(pa::launch_gather_read_probe(base, ids, num_chunks, chunk_bytes, sink, grid,
+                                                 (hipStream_t)stream));
+}
+
+int pa_set_decode_kernel(int choice) {
+  return pa::set_decode_kernel(choice) == 0 ? PA_OK : PA_ERR_UNSUPPORTED;
+}
+
+int pa_get_decode_kernel(void) { return pa::get_decode_kernel(); }
+
+const char* pa_decode_kernel_name(int kv_dtype, int num_q_heads, int num_kv_heads) {
+  if (kv_dtype != PA_F32 && kv_dtype != PA_BF16 && kv_dtype != PA_FP8_E4M3) return "";
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads) return "";
+  const int G = num_q_heads / num_kv_heads;
+  if (!group_supported(kv_dtype, G)) return "";
+  return pa::decode_uses_mfma(kv_dtype, G) ? "mfma" : "valu";
+}
+
 const char* pa_status_string(int status) {
   switch (status) {
     case PA_OK: return "ok";
     case PA_ERR_NULL: return "a required pointer is NULL";
     case PA_ERR_DTYPE: return "unsupported dtype or (query, KV) dtype pair";
     case PA_ERR_SHAPE: return "invalid size or head counts";
-    case PA_ERR_UNSUPPORTED: return "head_dim, block_size or GQA group size not supported";
+    case PA_ERR_UNSUPPORTED: return "head_dim, block_size, GQA group size or kernel choice not supported";
     case PA_ERR_PARTITION: return "invalid partition_size or max_num_partitions";
     case PA_ERR_HIP: return "HIP kernel launch failed";
     case PA_ERR_ALIGN: return "a buffer is not 16-byte aligned";

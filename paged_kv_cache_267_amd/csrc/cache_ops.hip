@@ -44,14 +44,15 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
 }
 
 // Merge of per-partition results by their log-sum-exp: for each (sequence,
-// query head) with keys [lo, L), partitions p with [pP, (p+1)P) meeting that
+// query head) with keys [lo, L), the partitions p with [pP, (p+1)P) meeting that
 // range are combined as sum_p e^(lse_p - M) o_p / sum_p e^(lse_p - M).
-// One 256-thread workgroup per row: the weights go to LDS, then thread t sums
-// float4 column t % (D/4) over partitions t / (D/4), t / (D/4) + SLOTS, ...
-// so 8 (D = 128) or 16 (D = 64) partitions are read at once, and the slots
-// are folded through LDS at the end.
+// One 256-thread workgroup per row.  Thread t owns float4 column t % (D/4) of
+// the partitions t / (D/4) + k * SLOTS: per round it issues all RED_LOADS of
+// its partial-output loads and their LSE loads at once (RED_LOADS * SLOTS = 128
+// partitions per round, so a 64K-token sequence split at 512 is one round),
+// keeps a running max of its own, and the slots are folded through LDS at the
+// end with their maxima.
 constexpr int RED_THREADS = 256;
-constexpr int RED_CHUNK = 1024;  // partitions whose weights are staged at a time
 
 template <bool OUT_BF16, int D>
 __global__ __launch_bounds__(RED_THREADS) void reduce_lse_kernel(
@@ -60,61 +61,70 @@ __global__ __launch_bounds__(RED_THREADS) void reduce_lse_kernel(
     int max_parts, int window) {
   constexpr int COLS = D / 4;                 // float4 columns per partition
   constexpr int SLOTS = RED_THREADS / COLS;   // partitions read in parallel
-  __shared__ float w_s[RED_CHUNK];
-  __shared__ float red[RED_THREADS / 64];
+  constexpr int RED_LOADS = 128 / SLOTS;      // loads per thread per round
+  __shared__ float m_s[SLOTS], den_s[SLOTS];
   __shared__ float4 acc_s[SLOTS][COLS];
   const int hq = blockIdx.x, s = blockIdx.y, t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
+  const int col = t % COLS, slot = t / COLS;
   int L = seq_lens[s];
   L = L < 0 ? 0 : L;
   const int lo = (window > 0 && L > window) ? L - window : 0;
   const int p_lo = lo / partition_size;
-  const int p_hi = min(max_parts, (L + partition_size - 1) / partition_size);
+  const int p_hi = L > 0 ? min(max_parts, (L + partition_size - 1) / partition_size) : p_lo;
   const size_t row = (size_t)s * Hq + hq;
   const float* lse = part_lse + row * max_parts;
+  const float* po = part_out + row * max_parts * D + 4 * col;
 
-  // M = max over the row's partitions
-  float mx = -INFINITY;
-  for (int q = p_lo + t; q < p_hi; q += RED_THREADS) mx = fmaxf(mx, lse[q]);
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-
-  const int col = t % COLS, slot = t / COLS;
+  float m = -INFINITY, den = 0.f;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  float den = 0.f;
-  if (L > 0 && mx != -INFINITY) {
-    for (int c0 = p_lo; c0 < p_hi; c0 += RED_CHUNK) {
-      const int c1 = min(p_hi, c0 + RED_CHUNK);
-      __syncthreads();
-      for (int q = c0 + t; q < c1; q += RED_THREADS) {
-        const float l = lse[q];
-        w_s[q - c0] = l == -INFINITY ? 0.f : __expf(l - mx);
-      }
-      __syncthreads();
-      if (t < COLS)
-        for (int q = c0; q < c1; ++q) den += w_s[q - c0];
-#pragma unroll 4
-      for (int q = c0 + slot; q < c1; q += SLOTS) {
-        const float w = w_s[q - c0];
-        if (w != 0.f) {  // skipped partitions may hold anything
-          const float4 o = *(const float4*)(part_out + (row * max_parts + q) * D + 4 * col);
-          a.x += w * o.x; a.y += w * o.y; a.z += w * o.z; a.w += w * o.w;
-        }
+  for (int q0 = p_lo + slot; q0 < p_hi; q0 += RED_LOADS * SLOTS) {
+    float l[RED_LOADS];
+    float4 o[RED_LOADS];
+#pragma unroll
+    for (int k = 0; k < RED_LOADS; ++k) {   // all loads of the round issue before any use
+      const int q = q0 + k * SLOTS;
+      l[k] = -INFINITY;
+      o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (q < p_hi) {
+        l[k] = lse[q];
+        o[k] = *(const float4*)(po + (size_t)q * D);
       }
     }
+    float cm = m;
+#pragma unroll
+    for (int k = 0; k < RED_LOADS; ++k) cm = fmaxf(cm, l[k]);
+    if (cm == -INFINITY) continue;
+    const float r = __expf(m - cm);   // m = -inf: r = 0 and a, den are still 0
+    den *= r;
+    a.x *= r; a.y *= r; a.z *= r; a.w *= r;
+#pragma unroll
+    for (int k = 0; k < RED_LOADS; ++k) {
+      const float w = __expf(l[k] - cm);   // -inf: 0
+      den += w;
+      a.x += w * o[k].x; a.y += w * o[k].y; a.z += w * o[k].z; a.w += w * o[k].w;
+    }
+    m = cm;
   }
+  if (col == 0) { m_s[slot] = m; den_s[slot] = den; }
   acc_s[slot][col] = a;
   __syncthreads();
   if (t < COLS) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < SLOTS; ++k) M = fmaxf(M, m_s[k]);
     float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k = 0; k < SLOTS; ++k) {
-      const float4 v = acc_s[k][t];
-      r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
+    float dsum = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < SLOTS; ++k) {
+        const float f = m_s[k] == -INFINITY ? 0.f : __expf(m_s[k] - M);
+        const float4 v = acc_s[k][t];
+        dsum += f * den_s[k];
+        r.x += f * v.x; r.y += f * v.y; r.z += f * v.z; r.w += f * v.w;
+      }
     }
-    if (den > 0.f) {
-      const float inv = 1.f / den;
+    if (dsum > 0.f) {
+      const float inv = 1.f / dsum;
       r.x *= inv; r.y *= inv; r.z *= inv; r.w *= inv;
     }
     if (OUT_BF16) {

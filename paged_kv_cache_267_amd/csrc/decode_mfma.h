@@ -37,11 +37,14 @@
 // waves take a segment's 16-token sub-tiles round-robin) two tiles ahead
 // across segment boundaries, with a fixed number of loads per step (a wave
 // past its last tile re-reads block 0), so every wait before a tile's first
-// use leaves the two younger tiles in flight.  Segment ends merge the 4 waves'
-// (max, sum, acc) through LDS behind barriers that order LDS only, and write
-// the output (unsplit) or the partition's output and natural-log LSE (split).
-// A segment longer than the staged table is carried into the next batch with
-// its running state.
+// use leaves the two younger tiles in flight.  At a segment end a wave
+// deposits its (max, sum, acc) in an LDS merge area and streams on; at its next
+// segment end (or after the batch's closing barrier) it merges a quarter of
+// that segment's output from the 4 deposits, in wave order, and writes it: the
+// output row (unsplit) or the partition's output and natural-log LSE (split).
+// Counters in LDS order deposits and merges, so no wave waits at a segment end
+// unless another wave is a whole segment behind.  A segment longer than the
+// staged table is carried into the next batch with its running state.
 #pragma once
 
 #include "common.h"
@@ -52,7 +55,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int MFMA_WAVES = 4;
-constexpr int MFMA_SEQ_CHUNK = 1024;   // sequences per launch (prefix kept in LDS)
+constexpr int MFMA_SEQ_CHUNK = 1024;   // sequences per launch (schedule kept in LDS)
 constexpr int MFMA_TBL = 2048;         // block-table entries staged per batch
 constexpr float LAZY_RESCALE_LOG2 = 8.0f;
 // register buffers per wave: NBUF - 1 sub-tiles in flight while one is
@@ -65,6 +68,9 @@ struct MfmaGeom {
   static constexpr int QBYTES = G <= 8 ? 16384 : 8192;     // LDS for staged queries
   static constexpr int SLOTS_RAW = QBYTES / (G * QROW * 2);
   static constexpr int SLOTS = SLOTS_RAW < 32 ? SLOTS_RAW : 32;  // segments per batch
+  // merge areas, used by successive segment ends in turn: two when they fit
+  // (then a wave never waits at a segment end), else one
+  static constexpr int NPAR = G <= 8 ? 2 : 1;
 };
 
 // Per-batch description of one segment slot.
@@ -90,11 +96,15 @@ struct MfmaSmem {
   uint16_t q[MfmaGeom<D, G>::SLOTS][G][MfmaGeom<D, G>::QROW];
   SegMeta meta[MfmaGeom<D, G>::SLOTS];
   int32_t bcount, bnext_m, bnext_st, scan[2][MFMA_WAVES];
-  float m[MFMA_WAVES][G];
-  float l[MFMA_WAVES][G];
+  int32_t arrived[MfmaGeom<D, G>::NPAR];  // deposits into each area (4 per use)
+  int32_t done[MfmaGeom<D, G>::NPAR];     // quarter merges out of each area (4 per use)
   union {
-    float acc[MFMA_WAVES][G][D + 4];   // merge area (rows padded: no bank conflicts)
-    int32_t pkey[MFMA_SORT_MAX];       // sort keys, before any merge
+    struct {
+      float m[MFMA_WAVES][G];
+      float l[MFMA_WAVES][G];
+      float acc[MFMA_WAVES][G][D + 4];    // rows padded: no bank conflicts
+    } area[MfmaGeom<D, G>::NPAR];
+    int32_t pkey[MFMA_SORT_MAX];          // sort keys, before any merge
   } u;
 };
 
@@ -235,6 +245,11 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
       if (tid + r * NTH < NPART) sm.plist[rk[r]] = mine[r];
     __syncthreads();
   }
+  if (tid < MfmaGeom<D, G>::NPAR) {
+    sm.arrived[tid] = 0;
+    sm.done[tid] = 0;
+  }
+  __syncthreads();
   const int total = F + NPART;
   // workgroup j takes list entries in serpentine order: round r gives it entry
   // r*J + j (r even) or r*J + J-1-j (r odd), so the largest entries of one
@@ -308,6 +323,56 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
     for (int nb = 0; nb < NB; ++nb) acc[nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     m_ref = -INFINITY;
     l_run = 0.f;
+  };
+
+  // segment ends this wave has passed (the same sequence in every wave), and
+  // the last one, whose quarter merge is still to do (pend_s < 0: none)
+  int uses = 0;
+  int pend_s = -1, pend_pp = 0, pend_par = 0, pend_gen = 0;
+
+  auto spin_until = [&](const int32_t* ctr, int target) {
+    while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target)
+      __builtin_amdgcn_s_sleep(1);
+  };
+  // Merge of the 4 waves' states of a finished segment, done by quarters: wave
+  // w combines (in wave order) and writes outputs [w, w+1) * G*D/4 of the
+  // segment's G x D block.
+  auto merge_quarter = [&]() {
+    if (pend_s < 0) return;
+    constexpr int QN = G * D / MFMA_WAVES;
+    const int par = pend_par;
+    spin_until(&sm.arrived[par], MFMA_WAVES * (pend_gen + 1));
+    auto& ar = sm.u.area[par];
+#pragma unroll
+    for (int i0 = 0; i0 < QN; i0 += 64) {
+      const int e = wave * QN + i0 + lane;
+      if (QN % 64 == 0 || i0 + lane < QN) {
+        const int g = e / D, d = e % D;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < MFMA_WAVES; ++w) mx = fmaxf(mx, ar.m[w][g]);
+        float den = 0.f, num = 0.f;
+#pragma unroll
+        for (int w = 0; w < MFMA_WAVES; ++w) {
+          const float f =
+              (mx == -INFINITY || ar.m[w][g] == -INFINITY) ? 0.f : fast_exp2(ar.m[w][g] - mx);
+          den += f * ar.l[w][g];
+          num += f * ar.acc[w][g][d];
+        }
+        const float o = den > 0.f ? num * (p.v_scale / den) : 0.f;
+        const size_t r = (size_t)pend_s * Hq + hk * G + g;
+        if (p.part_out == nullptr) {
+          ((uint16_t*)p.out)[r * D + d] = to_bf16_bits(o);
+        } else {
+          const size_t pi = r * p.max_parts + pend_pp;
+          p.part_out[pi * D + d] = o;
+          if (d == 0) p.part_lse[pi] = (mx + __log2f(den)) * 0.69314718055994531f;
+        }
+      }
+    }
+    if (lane == 0)
+      __hip_atomic_fetch_add(&sm.done[par], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    pend_s = -1;
   };
 
   int bm = 0, bst = -1;  // next batch starts at segment bm, sub-tile bst (-1: its start)
@@ -509,47 +574,35 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
       }
     };
 
-    // ---- segment ends: merge the 4 waves and write (only slots with fin = 1) ------------
+    // ---- segment ends (slots with fin = 1) ------------------------------------------------
+    // A wave first does its quarter of the previous segment's merge (all waves
+    // have deposited that one once they are past it), then deposits its own
+    // (max, sum, acc) in the next merge area and goes on streaming: no wave
+    // waits for another unless it is a whole segment ahead.
     auto finish_slot = [&](int c) {
       if (!uniform(sm.meta[c].fin)) return;  // continues in the next batch
+      constexpr int NPAR = MfmaGeom<D, G>::NPAR;
+      merge_quarter();
+      const int par = uses % NPAR, gen = uses / NPAR;
+      ++uses;
+      spin_until(&sm.done[par], MFMA_WAVES * gen);   // the area's previous use is merged
+      auto& ar = sm.u.area[par];
       const float l_col = colsum4(l_run);
       if (col < G) {
         if (row == 0) {
-          sm.m[wave][col] = m_ref;
-          sm.l[wave][col] = l_col;
+          ar.m[wave][col] = m_ref;
+          ar.l[wave][col] = l_col;
         }
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          *(f32x4_t*)&sm.u.acc[wave][col][16 * nb + 4 * row] = acc[nb];
+        for (int nb = 0; nb < NB; ++nb) *(f32x4_t*)&ar.acc[wave][col][16 * nb + 4 * row] = acc[nb];
       }
-      lds_barrier();
-      const int s = s0 + uniform(sm.meta[c].s), pp = uniform(sm.meta[c].p);
-      for (int i = tid; i < G * D; i += NTH) {
-        const int g = i / D, d = i % D;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < MFMA_WAVES; ++w) mx = fmaxf(mx, sm.m[w][g]);
-        float den = 0.f, num = 0.f;
-        if (mx != -INFINITY) {
-#pragma unroll
-          for (int w = 0; w < MFMA_WAVES; ++w) {
-            const float f = sm.m[w][g] == -INFINITY ? 0.f : fast_exp2(sm.m[w][g] - mx);
-            den += f * sm.l[w][g];
-            num += f * sm.u.acc[w][g][d];
-          }
-        }
-        const float o = den > 0.f ? num / den * p.v_scale : 0.f;
-        const int hq = hk * G + g;
-        if (p.part_out == nullptr) {
-          ((uint16_t*)p.out)[((size_t)s * Hq + hq) * D + d] = to_bf16_bits(o);
-        } else {
-          const size_t pi = ((size_t)s * Hq + hq) * p.max_parts + pp;
-          p.part_out[pi * D + d] = o;
-          if (d == 0) p.part_lse[pi] = (mx + __log2f(den)) * 0.69314718055994531f;
-        }
-      }
-      lds_barrier();
+      if (lane == 0)
+        __hip_atomic_fetch_add(&sm.arrived[par], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       reset();
+      pend_s = s0 + uniform(sm.meta[c].s);
+      pend_pp = uniform(sm.meta[c].p);
+      pend_par = par;
+      pend_gen = gen;
     };
 
     // ---- main loop: NBUF buffers, NBUF - 1 tiles in flight --------------------------------
@@ -579,6 +632,7 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
     }
   stream_done:
     __syncthreads();           // the next batch plan overwrites the staged tables
+    merge_quarter();           // every wave has deposited the batch's last segment
   }
 }
 

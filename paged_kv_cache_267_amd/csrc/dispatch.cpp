@@ -3,11 +3,31 @@
 
 #include "../../include/pa.h"
 
+#include <atomic>
+
 namespace pa {
 
-// The matrix cores take groups of 8 or more query heads per KV head; smaller
-// groups use the VALU bandwidth path (f32 caches always do).
-bool decode_uses_mfma(int kv_dtype, int G) { return kv_dtype != PA_F32 && G >= 8; }
+static std::atomic<int> g_choice{PA_KERNEL_AUTO};
+
+int set_decode_kernel(int choice) {
+  if (choice != PA_KERNEL_AUTO && choice != PA_KERNEL_VALU && choice != PA_KERNEL_MFMA) return -1;
+  g_choice.store(choice, std::memory_order_relaxed);
+  return 0;
+}
+int get_decode_kernel() { return g_choice.load(std::memory_order_relaxed); }
+
+// Automatic choice: the matrix cores take groups of 8 or more query heads per
+// KV head; smaller groups use the VALU bandwidth path (f32 caches always do).
+// Groups of 16 exist only on the matrix cores.
+bool decode_uses_mfma(int kv_dtype, int G) {
+  if (kv_dtype == PA_F32) return false;
+  if (G > 8) return true;
+  switch (get_decode_kernel()) {
+    case PA_KERNEL_VALU: return false;
+    case PA_KERNEL_MFMA: return true;
+    default: return G >= 8;
+  }
+}
 
 hipError_t dispatch_decode(const DecodeParams& p, int kv_dtype, int D, int BS, int G, int parts,
                            hipStream_t stream) {

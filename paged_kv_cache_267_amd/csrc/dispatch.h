@@ -26,7 +26,13 @@ hipError_t decode_mfma_bf16(const DecodeParams& p, int D, int BS, int G, int par
 hipError_t decode_mfma_fp8(const DecodeParams& p, int D, int BS, int G, int parts,
                            hipStream_t stream);
 
-// True when the matrix-core kernel serves (KV dtype, group size).
+// Process-wide kernel-family choice (pa_kernel_choice); set returns -1 for an
+// unknown value.
+int set_decode_kernel(int choice);
+int get_decode_kernel();
+
+// True when the matrix-core kernel serves (KV dtype, group size) under the
+// current choice.
 bool decode_uses_mfma(int kv_dtype, int G);
 
 // Chooses the kernel family for (KV dtype, group size) and launches it with a
@@ -40,6 +46,9 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc
 hipError_t launch_reduce_lse(const float* part_out, const float* part_lse,
                              const int32_t* seq_lens, int S, int Hq, int D, int P, int max_parts,
                              int window, void* out, bool out_bf16, hipStream_t stream);
+hipError_t launch_gather_read_probe(const void* base, const int32_t* ids, long long num_chunks,
+                                    int chunk_bytes, unsigned* sink, int grid,
+                                    hipStream_t stream);
 hipError_t launch_fp8_dequant(const uint8_t* codes, float scale, float* out, long long n,
                               hipStream_t stream);
 

@@ -122,3 +122,37 @@ def test_workspace_bytes():
 def test_status_strings():
     for s in range(8):
         assert pa.lib().pa_status_string(s)
+
+
+def test_decode_kernel_choice():
+    L = pa.lib()
+    assert pa.pa_get_decode_kernel() == "auto"
+    # automatic choice: matrix cores for groups of 8 or more, never for f32 caches
+    assert pa.pa_decode_kernel_name(pa.PA_BF16, 32, 8) == "valu"
+    assert pa.pa_decode_kernel_name(pa.PA_BF16, 64, 8) == "mfma"
+    assert pa.pa_decode_kernel_name(pa.PA_FP8_E4M3, 128, 8) == "mfma"
+    assert pa.pa_decode_kernel_name(pa.PA_F32, 64, 8) == "valu"
+    with pa.decode_kernel("mfma"):
+        assert pa.pa_decode_kernel_name(pa.PA_BF16, 8, 8) == "mfma"
+        assert pa.pa_decode_kernel_name(pa.PA_F32, 8, 8) == "valu"
+    with pa.decode_kernel("valu"):
+        assert pa.pa_decode_kernel_name(pa.PA_FP8_E4M3, 64, 8) == "valu"
+        assert pa.pa_decode_kernel_name(pa.PA_BF16, 32, 2) == "mfma"   # G = 16
+    assert pa.pa_get_decode_kernel() == "auto"
+    # unsupported combinations and values
+    assert pa.pa_decode_kernel_name(pa.PA_F32, 128, 8) == ""      # G = 16 needs bf16 / fp8
+    assert pa.pa_decode_kernel_name(pa.PA_BF16, 24, 8) == ""      # G = 3
+    assert pa.pa_decode_kernel_name(pa.PA_BF16, 30, 8) == ""      # not a multiple
+    assert pa.pa_decode_kernel_name(7, 8, 8) == ""
+    assert L.pa_set_decode_kernel(3) == 4 and L.pa_set_decode_kernel(-1) == 4
+    assert pa.pa_get_decode_kernel() == "auto"
+
+
+def test_probe_validation():
+    L = pa.lib()
+    assert L.pa_probe_gather_read(A, A, 0, 4096, A, 0, NULL) == 0        # no-op
+    assert L.pa_probe_gather_read(A, A, 4, 3000, A, 0, NULL) == 3        # not a power of two
+    assert L.pa_probe_gather_read(A, A, 4, 512, A, 0, NULL) == 3         # below 1 KiB
+    assert L.pa_probe_gather_read(A, A, -1, 4096, A, 0, NULL) == 3
+    assert L.pa_probe_gather_read(NULL, A, 4, 4096, A, 0, NULL) == 1
+    assert L.pa_probe_gather_read(ODD, A, 4, 4096, A, 0, NULL) == 7

@@ -14,12 +14,21 @@ import numpy as np
 import pytest
 
 import oracle
+import paged_kv_cache_267_amd as pa
 from paged_kv_cache_267_amd import workloads as W
 from tests.helpers import err_stats, oracle_caches, oracle_decode, oracle_decode_split
 
 pytestmark = pytest.mark.gpu
 
 TOL = {"bf16": (1e-2, 1e-3), "fp8_e4m3": (2e-2, 2e-3), "f32": (1e-4, 1e-5)}
+
+
+def kernels(kvdt, G=1):
+    """Decode kernel families that serve a KV dtype and group size (f32 caches:
+    VALU only; groups of 16: MFMA only)."""
+    if kvdt == "f32":
+        return ["valu"]
+    return ["mfma"] if G > 8 else ["valu", "mfma"]
 
 
 def announce(msg):
@@ -131,48 +140,55 @@ def test_decode_small_parity(kvdt, D, bs, G, split):
     qdt = "f32" if kvdt == "f32" else "bf16"
     window = {2: 70, 16: 45}.get(G, 0)
     lens = [0, 1, 2, 15, 16, 17, 33, 100, 129, 300]
-    announce(f"decode {kvdt} D{D} bs{bs} G{G} split={split} window={window}")
     wl = W.random_case(1000 + D + bs + G, seq_lens=lens, num_q_heads=2 * G, num_kv_heads=2,
                        head_dim=D, block_size=bs, q_dtype=qdt, kv_dtype=kvdt,
                        sliding_window=window, partition_size=64)
-    dw = gpu_run(wl, split=split)
     kc, vc = oracle_caches(wl)
     ref = oracle_decode(wl, kc, vc)
-    assert_close(dw.out_f64(), ref, kvdt, "out")
-    # L = 0 rows are exact zeros
     L = np.repeat(wl.seq_lens, wl.num_q_heads)
-    assert np.all(dw.out_f64()[L == 0] == 0.0)
+    for k in kernels(kvdt, G):
+        announce(f"decode {kvdt} D{D} bs{bs} G{G} split={split} window={window} kernel={k}")
+        with pa.decode_kernel(k):
+            got = gpu_run(wl, split=split).out_f64()
+        assert_close(got, ref, kvdt, f"out ({k})")
+        assert np.all(got[L == 0] == 0.0)   # L = 0 rows are exact zeros
 
 
 @pytest.mark.parametrize("kvdt", ["bf16", "fp8_e4m3"])
 def test_split_partials_and_lse(kvdt):
     import torch
-    announce(f"split partials {kvdt}")
     wl = W.random_case(77, seq_lens=[0, 5, 64, 65, 200, 513, 2000], num_q_heads=8, num_kv_heads=2,
                        head_dim=128, block_size=16, kv_dtype=kvdt, sliding_window=150,
                        partition_size=64)
-    dw = gpu_run(wl, split=True)
     kc, vc = oracle_caches(wl)
-    po, pl = oracle_decode_split(wl, kc, vc, max_partitions=dw.max_parts)
-    g_lse = dw.part_lse.cpu().numpy().reshape(pl.shape).astype(np.float64)
-    g_po = dw.part_out.cpu().numpy().reshape(po.shape).astype(np.float64)
-    empty = np.isneginf(pl)          # partitions outside [lo, L): not written
-    assert np.isfinite(g_lse[~empty]).all()
-    np.testing.assert_allclose(g_lse[~empty], pl[~empty], rtol=0, atol=1e-4)
-    mx, _ = err_stats(g_po[~empty], po[~empty])
-    assert mx <= 1e-2
+    po = pl = None
+    for k in kernels(kvdt):
+        announce(f"split partials {kvdt} kernel={k}")
+        with pa.decode_kernel(k):
+            dw = gpu_run(wl, split=True)
+        if po is None:
+            po, pl = oracle_decode_split(wl, kc, vc, max_partitions=dw.max_parts)
+        g_lse = dw.part_lse.cpu().numpy().reshape(pl.shape).astype(np.float64)
+        g_po = dw.part_out.cpu().numpy().reshape(po.shape).astype(np.float64)
+        empty = np.isneginf(pl)          # partitions outside [lo, L): not written
+        assert np.isfinite(g_lse[~empty]).all()
+        np.testing.assert_allclose(g_lse[~empty], pl[~empty], rtol=0, atol=1e-4)
+        mx, _ = err_stats(g_po[~empty], po[~empty])
+        assert mx <= 1e-2, k
     del torch
 
 
 # ---------------------------------------------------------------------------
 # invariants on the device
 
-def test_gpu_block_permutation_bit_identical():
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_gpu_block_permutation_bit_identical(kernel):
     import torch
-    announce("gpu permutation invariance")
+    announce(f"gpu permutation invariance kernel={kernel}")
     wl = W.random_case(31, seq_lens=[3, 50, 77, 200], num_q_heads=8, num_kv_heads=2,
                        head_dim=128, block_size=16)
-    a = gpu_run(wl, split=True).out.clone()
+    with pa.decode_kernel(kernel):
+        a = gpu_run(wl, split=True).out.clone()
     # same logical content, physical ids relabelled by a permutation of the pool
     pi = np.random.default_rng(8).permutation(wl.num_blocks).astype(np.int32)
     bs = wl.block_size
@@ -180,17 +196,20 @@ def test_gpu_block_permutation_bit_identical():
     t2 = np.where(wl.block_tables >= 0, pi[np.maximum(wl.block_tables, 0)], -1).astype(np.int32)
     wl2 = dataclasses.replace(wl, block_tables=t2, hist_slots=relabel(wl.hist_slots),
                               new_slots=relabel(wl.new_slots))
-    b = gpu_run(wl2, split=True).out
+    with pa.decode_kernel(kernel):
+        b = gpu_run(wl2, split=True).out
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_gpu_prefix_aliasing_bit_identical():
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_gpu_prefix_aliasing_bit_identical(kernel):
     import torch
-    announce("gpu prefix aliasing invariance")
+    announce(f"gpu prefix aliasing invariance kernel={kernel}")
     wl = W.random_case(32, seq_lens=[40, 57, 33, 90], num_q_heads=8, num_kv_heads=2,
                        head_dim=128, block_size=16, shared_prefix=32)
-    a = gpu_run(wl, split=False).out.clone()
+    with pa.decode_kernel(kernel):
+        a = gpu_run(wl, split=False).out.clone()
     # give every sequence after the first its own copy of the prefix blocks
     spare = wl.num_blocks
     t2 = wl.block_tables.copy()
@@ -208,7 +227,8 @@ def test_gpu_prefix_aliasing_bit_identical():
     wl2 = dataclasses.replace(wl, block_tables=t2, num_blocks=spare,
                               hist_key=np.concatenate(hist_k), hist_value=np.concatenate(hist_v),
                               hist_slots=np.concatenate(hist_s))
-    b = gpu_run(wl2, split=False).out
+    with pa.decode_kernel(kernel):
+        b = gpu_run(wl2, split=False).out
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
@@ -220,15 +240,19 @@ def test_gpu_len_one_and_window_one_exact(kvdt):
     wl = W.random_case(41, seq_lens=[1, 1, 1, 1], num_q_heads=4, num_kv_heads=2, head_dim=128,
                        block_size=16, q_dtype=qdt, kv_dtype=kvdt)
     kc, vc = oracle_caches(wl)
-    for split in (False, True):
-        got = gpu_run(wl, split=split).out_f64()
-        assert np.array_equal(got, oracle_decode(wl, kc, vc)), "L = 1 must return V row 0"
+    for k in kernels(kvdt):
+        for split in (False, True):
+            with pa.decode_kernel(k):
+                got = gpu_run(wl, split=split).out_f64()
+            assert np.array_equal(got, oracle_decode(wl, kc, vc)), f"L = 1 must return V row 0 ({k})"
     wl = W.random_case(42, seq_lens=[5, 16, 40, 99], num_q_heads=4, num_kv_heads=2, head_dim=128,
                        block_size=16, q_dtype=qdt, kv_dtype=kvdt, sliding_window=1)
     kc, vc = oracle_caches(wl)
-    for split in (False, True):
-        got = gpu_run(wl, split=split).out_f64()
-        assert np.array_equal(got, oracle_decode(wl, kc, vc)), "W = 1 must return V row L-1"
+    for k in kernels(kvdt):
+        for split in (False, True):
+            with pa.decode_kernel(k):
+                got = gpu_run(wl, split=split).out_f64()
+            assert np.array_equal(got, oracle_decode(wl, kc, vc)), f"W = 1 must return V row L-1 ({k})"
 
 
 def test_window_skips_blocks_before_window():
@@ -238,8 +262,11 @@ def test_window_skips_blocks_before_window():
                        poison_out_of_window=True)
     kc, vc = oracle_caches(wl)
     ref = oracle_decode(wl, kc, vc)
-    for split in (False, True):
-        assert_close(gpu_run(wl, split=split).out_f64(), ref, "fp8_e4m3", f"split={split}")
+    for k in kernels("fp8_e4m3"):
+        for split in (False, True):
+            with pa.decode_kernel(k):
+                got = gpu_run(wl, split=split).out_f64()
+            assert_close(got, ref, "fp8_e4m3", f"split={split} kernel={k}")
 
 
 # ---------------------------------------------------------------------------
@@ -261,26 +288,31 @@ def _rows_sample(wl, n, seed=0):
 def test_named_config_parity(cfg):
     announce(f"config {cfg}: generating")
     wl = W.config(cfg)
-    split = cfg != 1
-    announce(f"config {cfg} ({wl.name}): gpu step split={split}")
-    dw = gpu_run(wl, split=split)
-    got = dw.out_f64()
     announce(f"config {cfg}: oracle")
     rows = _rows_sample(wl, 4096 if cfg in (3, 5) else 1 << 30)
     kc, vc = oracle_caches(wl)
     ref = oracle_decode(wl, kc, vc, rows=rows)
-    if rows is not None:
-        got = got[rows]
-    assert_close(got, ref, wl.kv_dtype, f"config {cfg}")
-    if cfg == 4:  # the appended token went where the oracle put it
-        gk, gv = dw.cache_bytes()
-        assert np.array_equal(gk, kc.view(np.uint8)) and np.array_equal(gv, vc.view(np.uint8))
+    for k in kernels(wl.kv_dtype):
+        for split in ((False,) if cfg == 1 else (True, False)):
+            announce(f"config {cfg} ({wl.name}): gpu step split={split} kernel={k}")
+            with pa.decode_kernel(k):
+                dw = gpu_run(wl, split=split)
+            got = dw.out_f64()
+            if rows is not None:
+                got = got[rows]
+            assert_close(got, ref, wl.kv_dtype, f"config {cfg} split={split} kernel={k}")
+            if cfg == 4:  # the appended token went where the oracle put it
+                gk, gv = dw.cache_bytes()
+                assert np.array_equal(gk, kc.view(np.uint8)) and np.array_equal(gv, vc.view(np.uint8))
 
 
 def test_config5_window_poison_variant():
     announce("config 5 with out-of-window blocks pointing at a NaN block")
     wl = W.config(5, poison_out_of_window=True)
-    dw = gpu_run(wl, split=True)
     rows = _rows_sample(wl, 2048, seed=1)
     kc, vc = oracle_caches(wl)
-    assert_close(dw.out_f64()[rows], oracle_decode(wl, kc, vc, rows=rows), "fp8_e4m3", "cfg5-skip")
+    ref = oracle_decode(wl, kc, vc, rows=rows)
+    for k in kernels("fp8_e4m3"):
+        with pa.decode_kernel(k):
+            dw = gpu_run(wl, split=True)
+        assert_close(dw.out_f64()[rows], ref, "fp8_e4m3", f"cfg5-skip kernel={k}")
