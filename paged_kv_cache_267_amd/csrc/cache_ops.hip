@@ -46,32 +46,35 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
 // Merge of per-partition results by their log-sum-exp: for each (sequence,
 // query head) with keys [lo, L), the partitions p with [pP, (p+1)P) meeting that
 // range are combined as sum_p e^(lse_p - M) o_p / sum_p e^(lse_p - M).
-// One 256-thread workgroup per row.  Thread t owns float4 column t % (D/4) of
-// the partitions t / (D/4) + k * SLOTS: per round it issues all RED_LOADS of
-// its partial-output loads and their LSE loads at once (RED_LOADS * SLOTS = 128
-// partitions per round, so a 64K-token sequence split at 512 is one round),
-// keeps a running max of its own, and the slots are folded through LDS at the
-// end with their maxima.
+// WPR waves serve one row (1 for short rows: four rows per workgroup; 4 when a
+// row can span more partitions than one wave takes in a round).  Lane l of the
+// row's lanes owns float4 column l % (D/4) of the partitions l / (D/4) +
+// k * SLOTS: per round it issues all RED_LOADS of its partial-output loads and
+// their LSE loads at once and keeps a running max of its own; the lane groups
+// are folded with cross-lane swaps, then (WPR = 4) across waves through LDS.
 constexpr int RED_THREADS = 256;
+constexpr int RED_LOADS = 16;                // loads per lane per round
 
-template <bool OUT_BF16, int D>
+template <bool OUT_BF16, int D, int WPR>
 __global__ __launch_bounds__(RED_THREADS) void reduce_lse_kernel(
     const float* __restrict__ part_out, const float* __restrict__ part_lse,
-    const int32_t* __restrict__ seq_lens, void* __restrict__ out, int Hq, int partition_size,
-    int max_parts, int window) {
+    const int32_t* __restrict__ seq_lens, void* __restrict__ out, int rows, int Hq,
+    int partition_size, int max_parts, int window) {
   constexpr int COLS = D / 4;                 // float4 columns per partition
-  constexpr int SLOTS = RED_THREADS / COLS;   // partitions read in parallel
-  constexpr int RED_LOADS = 128 / SLOTS;      // loads per thread per round
-  __shared__ float m_s[SLOTS], den_s[SLOTS];
-  __shared__ float4 acc_s[SLOTS][COLS];
-  const int hq = blockIdx.x, s = blockIdx.y, t = threadIdx.x;
-  const int col = t % COLS, slot = t / COLS;
+  constexpr int SLOTS = 64 * WPR / COLS;      // partitions read in parallel by a row
+  constexpr int ROWS = RED_THREADS / 64 / WPR;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int r = blockIdx.x * ROWS + wave / WPR;
+  if (r >= rows) return;                      // whole row groups leave together
+  const int s = r / Hq;
+  const int rl = (wave % WPR) * 64 + lane;    // lane index within the row
+  const int col = rl % COLS, slot = rl / COLS;
   int L = seq_lens[s];
   L = L < 0 ? 0 : L;
   const int lo = (window > 0 && L > window) ? L - window : 0;
   const int p_lo = lo / partition_size;
   const int p_hi = L > 0 ? min(max_parts, (L + partition_size - 1) / partition_size) : p_lo;
-  const size_t row = (size_t)s * Hq + hq;
+  const size_t row = (size_t)r;
   const float* lse = part_lse + row * max_parts;
   const float* po = part_out + row * max_parts * D + 4 * col;
 
@@ -94,9 +97,9 @@ __global__ __launch_bounds__(RED_THREADS) void reduce_lse_kernel(
 #pragma unroll
     for (int k = 0; k < RED_LOADS; ++k) cm = fmaxf(cm, l[k]);
     if (cm == -INFINITY) continue;
-    const float r = __expf(m - cm);   // m = -inf: r = 0 and a, den are still 0
-    den *= r;
-    a.x *= r; a.y *= r; a.z *= r; a.w *= r;
+    const float f = __expf(m - cm);   // m = -inf: f = 0 and a, den are still 0
+    den *= f;
+    a.x *= f; a.y *= f; a.z *= f; a.w *= f;
 #pragma unroll
     for (int k = 0; k < RED_LOADS; ++k) {
       const float w = __expf(l[k] - cm);   // -inf: 0
@@ -105,35 +108,46 @@ __global__ __launch_bounds__(RED_THREADS) void reduce_lse_kernel(
     }
     m = cm;
   }
-  if (col == 0) { m_s[slot] = m; den_s[slot] = den; }
-  acc_s[slot][col] = a;
-  __syncthreads();
-  if (t < COLS) {
-    float M = -INFINITY;
+  // (m1, d1, a1) <- combination of (m1, d1, a1) and (m2, d2, a2)
+  auto combine = [](float& m1, float& d1, float4& a1, float m2, float d2, float4 a2) {
+    const float M = fmaxf(m1, m2);
+    const float f1 = m1 == -INFINITY ? 0.f : __expf(m1 - M);
+    const float f2 = m2 == -INFINITY ? 0.f : __expf(m2 - M);
+    d1 = f1 * d1 + f2 * d2;
+    a1.x = f1 * a1.x + f2 * a2.x; a1.y = f1 * a1.y + f2 * a2.y;
+    a1.z = f1 * a1.z + f2 * a2.z; a1.w = f1 * a1.w + f2 * a2.w;
+    m1 = M;
+  };
+  // fold the lane groups of a wave: lanes l and l + off hold the same column
 #pragma unroll
-    for (int k = 0; k < SLOTS; ++k) M = fmaxf(M, m_s[k]);
-    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
-    float dsum = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int k = 0; k < SLOTS; ++k) {
-        const float f = m_s[k] == -INFINITY ? 0.f : __expf(m_s[k] - M);
-        const float4 v = acc_s[k][t];
-        dsum += f * den_s[k];
-        r.x += f * v.x; r.y += f * v.y; r.z += f * v.z; r.w += f * v.w;
-      }
-    }
-    if (dsum > 0.f) {
-      const float inv = 1.f / dsum;
-      r.x *= inv; r.y *= inv; r.z *= inv; r.w *= inv;
+  for (int off = 32; off >= COLS; off >>= 1) {
+    const float4 a2 = make_float4(__shfl_xor(a.x, off, 64), __shfl_xor(a.y, off, 64),
+                                  __shfl_xor(a.z, off, 64), __shfl_xor(a.w, off, 64));
+    combine(m, den, a, __shfl_xor(m, off, 64), __shfl_xor(den, off, 64), a2);
+  }
+  if (WPR > 1) {   // fold the row's waves through LDS (one row per workgroup)
+    __shared__ float m_s[WPR][COLS], d_s[WPR][COLS];
+    __shared__ float4 a_s[WPR][COLS];
+    if (lane < COLS) { m_s[wave][lane] = m; d_s[wave][lane] = den; a_s[wave][lane] = a; }
+    __syncthreads();
+    if (wave != 0) return;
+    if (lane < COLS)
+      for (int w = 1; w < WPR; ++w) combine(m, den, a, m_s[w][lane], d_s[w][lane], a_s[w][lane]);
+  }
+  if (lane < COLS) {
+    if (den > 0.f) {
+      const float inv = 1.f / den;
+      a.x *= inv; a.y *= inv; a.z *= inv; a.w *= inv;
+    } else {
+      a = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     if (OUT_BF16) {
       uint2 b;
-      b.x = pack_bf16x2(r.x, r.y);
-      b.y = pack_bf16x2(r.z, r.w);
-      *(uint2*)((uint16_t*)out + row * D + 4 * t) = b;
+      b.x = pack_bf16x2(a.x, a.y);
+      b.y = pack_bf16x2(a.z, a.w);
+      *(uint2*)((uint16_t*)out + row * D + 4 * lane) = b;
     } else {
-      *(float4*)((float*)out + row * D + 4 * t) = r;
+      *(float4*)((float*)out + row * D + 4 * lane) = a;
     }
   }
 }
@@ -174,24 +188,50 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc
   return hipGetLastError();
 }
 
+template <bool OUT_BF16, int D, int WPR>
+static void launch_reduce_rows(const float* part_out, const float* part_lse,
+                               const int32_t* seq_lens, int rows, int Hq, int P, int max_parts,
+                               int window, void* out, hipStream_t stream) {
+  constexpr int ROWS = RED_THREADS / 64 / WPR;
+  hipLaunchKernelGGL((reduce_lse_kernel<OUT_BF16, D, WPR>), dim3((rows + ROWS - 1) / ROWS),
+                     dim3(RED_THREADS), 0, stream, part_out, part_lse, seq_lens, out, rows, Hq, P,
+                     max_parts, window);
+}
+
+template <bool OUT_BF16, int D>
+static void launch_reduce_d(const float* part_out, const float* part_lse,
+                            const int32_t* seq_lens, int rows, int Hq, int P, int max_parts,
+                            int window, void* out, hipStream_t stream) {
+  // partitions a row can meet: all of them, or those a window can touch
+  int span = max_parts;
+  if (window > 0) span = min(span, (window + P - 1) / P + 1);
+  // one wave takes 16 * (64 / (D / 4)) partitions per round
+  if (span > RED_LOADS * (256 / D))
+    launch_reduce_rows<OUT_BF16, D, 4>(part_out, part_lse, seq_lens, rows, Hq, P, max_parts,
+                                       window, out, stream);
+  else
+    launch_reduce_rows<OUT_BF16, D, 1>(part_out, part_lse, seq_lens, rows, Hq, P, max_parts,
+                                       window, out, stream);
+}
+
 hipError_t launch_reduce_lse(const float* part_out, const float* part_lse,
                              const int32_t* seq_lens, int S, int Hq, int D, int P, int max_parts,
                              int window, void* out, bool out_bf16, hipStream_t stream) {
-  dim3 grid(Hq, S), block(RED_THREADS);
+  const int rows = S * Hq;
   if (D == 128) {
     if (out_bf16)
-      hipLaunchKernelGGL((reduce_lse_kernel<true, 128>), grid, block, 0, stream, part_out,
-                         part_lse, seq_lens, out, Hq, P, max_parts, window);
+      launch_reduce_d<true, 128>(part_out, part_lse, seq_lens, rows, Hq, P, max_parts, window,
+                                 out, stream);
     else
-      hipLaunchKernelGGL((reduce_lse_kernel<false, 128>), grid, block, 0, stream, part_out,
-                         part_lse, seq_lens, out, Hq, P, max_parts, window);
+      launch_reduce_d<false, 128>(part_out, part_lse, seq_lens, rows, Hq, P, max_parts, window,
+                                  out, stream);
   } else {
     if (out_bf16)
-      hipLaunchKernelGGL((reduce_lse_kernel<true, 64>), grid, block, 0, stream, part_out,
-                         part_lse, seq_lens, out, Hq, P, max_parts, window);
+      launch_reduce_d<true, 64>(part_out, part_lse, seq_lens, rows, Hq, P, max_parts, window,
+                                out, stream);
     else
-      hipLaunchKernelGGL((reduce_lse_kernel<false, 64>), grid, block, 0, stream, part_out,
-                         part_lse, seq_lens, out, Hq, P, max_parts, window);
+      launch_reduce_d<false, 64>(part_out, part_lse, seq_lens, rows, Hq, P, max_parts, window,
+                                 out, stream);
   }
   return hipGetLastError();
 }

@@ -61,6 +61,8 @@ constexpr float LAZY_RESCALE_LOG2 = 8.0f;
 // register buffers per wave: NBUF - 1 sub-tiles in flight while one is
 // computed (E4M3 sub-tiles are half the bytes, so twice as many)
 template <int KV> struct MfmaDepth { static constexpr int NBUF = KV == KV_FP8 ? 5 : 3; };
+// query operand: kept in registers per segment (true) or read from LDS per tile
+constexpr bool MFMA_QREG = true;
 
 template <int D, int G>
 struct MfmaGeom {
@@ -85,26 +87,30 @@ struct SegMeta {
 };
 
 constexpr int MFMA_SORT_MAX = 512;     // partial segments ordered by size (more: by sequence)
+constexpr int MFMA_SIZE_CLASSES = 64;  // size classes of that order (one per lane of a wave)
 
 template <int D, int G>
 struct MfmaSmem {
   int32_t lens[MFMA_SEQ_CHUNK];        // clamped lengths
   int32_t fpre[MFMA_SEQ_CHUNK + 1];    // full partitions before each sequence (exclusive)
   int32_t ppre[MFMA_SEQ_CHUNK + 1];    // partial segments before each sequence (exclusive)
-  int32_t plist[MFMA_SORT_MAX];        // partial segments, largest first: (s << 20) | p
+  alignas(16) int32_t plist[MFMA_SORT_MAX];  // partial segments, largest first: (s << 20) | p
   int32_t tbl[MFMA_TBL];               // staged block ids of the batch
   uint16_t q[MfmaGeom<D, G>::SLOTS][G][MfmaGeom<D, G>::QROW];
   SegMeta meta[MfmaGeom<D, G>::SLOTS];
   int32_t bcount, bnext_m, bnext_st, scan[2][MFMA_WAVES];
   int32_t arrived[MfmaGeom<D, G>::NPAR];  // deposits into each area (4 per use)
   int32_t done[MfmaGeom<D, G>::NPAR];     // quarter merges out of each area (4 per use)
-  union {
+  union alignas(16) {
     struct {
       float m[MFMA_WAVES][G];
       float l[MFMA_WAVES][G];
       float acc[MFMA_WAVES][G][D + 4];    // rows padded: no bank conflicts
     } area[MfmaGeom<D, G>::NPAR];
-    int32_t pkey[MFMA_SORT_MAX];          // sort keys, before any merge
+    struct {                              // ordering of the partial segments, before any merge
+      int32_t cls[MFMA_SORT_MAX];
+      int32_t cnt[MFMA_SORT_MAX / 64][MFMA_SIZE_CLASSES];
+    } srt;
   } u;
 };
 
@@ -204,8 +210,16 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
   const int F = uniform(sm.fpre[S]), NPART = uniform(sm.ppre[S]);
   const bool sorted = NPART <= MFMA_SORT_MAX;
   if (sorted) {
-    // list the partial segments with their sizes, then place each by its rank
-    // under (size desc, sequence asc, partition asc)
+    // list the partial segments with a size class (4 classes per octave;
+    // larger segments get smaller classes), then order them by class with a
+    // stable counting sort, so every workgroup derives the same order
+    constexpr int NBK = MFMA_SIZE_CLASSES, CHUNKS = MFMA_SORT_MAX / 64, SR = MFMA_SORT_MAX / NTH;
+    auto size_class = [](int sz) -> int {
+      if (sz <= 0) return NBK - 1;
+      const int lz = 31 - __builtin_clz(sz);
+      const int c = lz >= 2 ? 4 * lz + ((sz >> (lz - 2)) & 3) : sz;
+      return NBK - 1 - min(NBK - 1, c);
+    };
     for (int i = tid; i < S; i += NTH) {
       const int L = sm.lens[i];
       int nf, np, f0;
@@ -219,30 +233,56 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
           seg_range(L, pp, t0, t1);
           if (P != 0 && t1 - t0 == P) continue;
           sm.plist[o] = (i << 20) | pp;
-          sm.u.pkey[o] = t1 - t0;
+          sm.u.srt.cls[o] = size_class(t1 - t0);
           ++o;
         }
       }
     }
+    for (int i = tid; i < CHUNKS * NBK; i += NTH) (&sm.u.srt.cnt[0][0])[i] = 0;
     __syncthreads();
-    int mine[MFMA_SORT_MAX / NTH], rk[MFMA_SORT_MAX / NTH], ky[MFMA_SORT_MAX / NTH];
+    // entry e sits in chunk e / 64 (one wave's lanes); its rank among the
+    // chunk's entries of its class comes from one ballot per class present
+    int mine[SR], cls[SR], wr[SR];
 #pragma unroll
-    for (int r = 0; r < MFMA_SORT_MAX / NTH; ++r) {
-      const int e = tid + r * NTH;
-      mine[r] = e < NPART ? sm.plist[e] : 0;
-      ky[r] = e < NPART ? sm.u.pkey[e] : 0;
-      rk[r] = 0;
+    for (int r = 0; r < SR; ++r) {
+      const int e = tid + r * NTH, c = wave + r * (NTH / 64);
+      const bool valid = e < NPART;
+      mine[r] = valid ? sm.plist[e] : 0;
+      cls[r] = valid ? sm.u.srt.cls[e] : NBK;
+      wr[r] = 0;
+      uint64_t todo = __builtin_amdgcn_ballot_w64(valid);
+      while (todo) {
+        const int k = __builtin_amdgcn_readlane(cls[r], (int)__builtin_ctzll(todo));
+        const uint64_t m = __builtin_amdgcn_ballot_w64(cls[r] == k);
+        if (cls[r] == k) wr[r] = __builtin_popcountll(m & ((1ull << lane) - 1));
+        if (lane == 0) sm.u.srt.cnt[c][k] = __builtin_popcountll(m);
+        todo &= ~m;
+      }
     }
-    for (int f = 0; f < NPART; ++f) {
-      const int kf = sm.u.pkey[f], vf = sm.plist[f];
+    __syncthreads();
+    // class starts (exclusive scan over classes of the chunk totals), then each
+    // chunk's base within its class, written over the counts
+    if (wave == 0) {
+      int tot = 0;
+      for (int c = 0; c < CHUNKS; ++c) tot += sm.u.srt.cnt[c][lane];
+      int x = tot;
 #pragma unroll
-      for (int r = 0; r < MFMA_SORT_MAX / NTH; ++r)
-        rk[r] += (kf > ky[r] || (kf == ky[r] && vf < mine[r])) ? 1 : 0;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+      }
+      int run = x - tot;
+      for (int c = 0; c < CHUNKS; ++c) {
+        const int n = sm.u.srt.cnt[c][lane];
+        sm.u.srt.cnt[c][lane] = run;
+        run += n;
+      }
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < MFMA_SORT_MAX / NTH; ++r)
-      if (tid + r * NTH < NPART) sm.plist[rk[r]] = mine[r];
+    for (int r = 0; r < SR; ++r)
+      if (tid + r * NTH < NPART)
+        sm.plist[sm.u.srt.cnt[wave + r * (NTH / 64)][cls[r]] + wr[r]] = mine[r];
     __syncthreads();
   }
   if (tid < MfmaGeom<D, G>::NPAR) {
@@ -495,6 +535,7 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
     };
 
     auto q_to_regs = [&](int c) {
+      if (!MFMA_QREG) return;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int d0 = (KV == KV_BF16) ? 32 * ks + 8 * row : 16 * (row + 4 * (ks >> 1)) + 8 * (ks & 1);
@@ -505,6 +546,16 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
     };
 
     auto compute_tile = [&](Buf& b) {
+      if (!MFMA_QREG) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int d0 =
+              (KV == KV_BF16) ? 32 * ks + 8 * row : 16 * (row + 4 * (ks >> 1)) + 8 * (ks & 1);
+          uint4 v = make_uint4(0, 0, 0, 0);
+          if (col < G) v = *(const uint4*)&sm.q[b.slot][col][d0];
+          qop[ks] = __builtin_bit_cast(bf16x8_t, (u32x4_t){v.x, v.y, v.z, v.w});
+        }
+      }
       f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < KL; ++i) {

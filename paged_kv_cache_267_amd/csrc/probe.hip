@@ -1,6 +1,6 @@
 // probe.hip -- a bandwidth probe with the decode kernels' access pattern:
-// whole chunks (the size of one (block, head) K or V tile) read with 16-byte
-// non-temporal loads, in the order of a chunk-id list.  With a random
+// whole chunks (the size of one (block, head) K or V tile) read by one wave
+// each with 16-byte non-temporal loads, in the order of a chunk-id list.  With a random
 // permutation it measures what HBM delivers to a paged gather; with ids in
 // order, a plain streaming read.  Nothing is computed but an XOR of the data,
 // which goes to one word so the loads cannot be dropped.
@@ -9,26 +9,32 @@
 namespace pa {
 
 constexpr int PROBE_THREADS = 256;
-constexpr int PROBE_DEPTH = 8;   // 16-byte loads per thread in flight
+constexpr int PROBE_DEPTH = 4;   // 1 KiB loads per wave in flight
 
-// A wave reads one 1 KiB row per load (64 lanes x 16 bytes); chunk k holds
-// rows [k << rpc_log2, (k + 1) << rpc_log2).  Row indices are wave-uniform,
-// so the chunk lookup is scalar work.
+// Each wave reads whole chunks, one 1 KiB row per load (64 lanes x 16 bytes),
+// as a decode wave reads a K or V tile: wave w of the grid takes list entries
+// w, w + W, w + 2W, ... (W waves in the grid), and its rows run through them
+// in order, PROBE_DEPTH rows per round.  Row indices are wave-uniform, so the
+// chunk lookup is scalar work.
 __global__ __launch_bounds__(PROBE_THREADS) void gather_read_probe_kernel(
-    const uint8_t* __restrict__ base, const int32_t* __restrict__ ids, long long rows,
+    const uint8_t* __restrict__ base, const int32_t* __restrict__ ids, long long num_chunks,
     int rpc_log2, unsigned* __restrict__ sink) {
-  constexpr int WAVES = PROBE_THREADS / 64;
-  const int lane = threadIdx.x & 63, wave = wave_id();
-  const long long round = (long long)WAVES * PROBE_DEPTH;   // rows per workgroup round
+  const int lane = threadIdx.x & 63;
+  const long long nw = (long long)gridDim.x * (PROBE_THREADS / 64);
+  const long long w = (long long)blockIdx.x * (PROBE_THREADS / 64) + wave_id();
+  const long long mine = w < num_chunks ? (num_chunks - 1 - w) / nw + 1 : 0;  // chunks of this wave
+  const long long rows = mine << rpc_log2;
+  const long long rmask = (1ll << rpc_log2) - 1;
   unsigned x = 0;
-  for (long long r0 = (long long)blockIdx.x * round; r0 < rows; r0 += (long long)gridDim.x * round) {
+  for (long long r0 = 0; r0 < rows; r0 += PROBE_DEPTH) {
     uint4 v[PROBE_DEPTH];
 #pragma unroll
     for (int i = 0; i < PROBE_DEPTH; ++i) {
-      long long w = r0 + (long long)i * WAVES + wave;
-      if (w >= rows) w = rows - 1;
-      const long long k = w >> rpc_log2, o = w & ((1ll << rpc_log2) - 1);
-      const size_t off = (((size_t)ids[k] << rpc_log2) + (size_t)o) * 1024 + (size_t)lane * 16;
+      long long n = r0 + i;
+      if (n >= rows) n = rows - 1;
+      const long long k = w + (n >> rpc_log2) * nw;
+      const size_t off = (((size_t)ids[k] << rpc_log2) + (size_t)(n & rmask)) * 1024 +
+                         (size_t)lane * 16;
       v[i] = load_nt16(base + off);
     }
 #pragma unroll
@@ -45,7 +51,7 @@ hipError_t launch_gather_read_probe(const void* base, const int32_t* ids, long l
   int rpc_log2 = 0;
   while ((1024 << rpc_log2) < chunk_bytes) ++rpc_log2;
   hipLaunchKernelGGL(gather_read_probe_kernel, dim3(grid), dim3(PROBE_THREADS), 0, stream,
-                     (const uint8_t*)base, ids, num_chunks << rpc_log2, rpc_log2, sink);
+                     (const uint8_t*)base, ids, num_chunks, rpc_log2, sink);
   return hipGetLastError();
 }
 

@@ -178,6 +178,26 @@ def test_split_partials_and_lse(kvdt):
     del torch
 
 
+@pytest.mark.parametrize("kvdt,D", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("window", [0, 300])
+def test_reduce_many_partitions(kvdt, D, window):
+    """Rows spanning up to 132 partitions of 16 tokens: more than one wave of the
+    merge takes in a round (without a window), so the rows are split across
+    waves; with the window the short-row form serves the same sizes."""
+    qdt = "f32" if kvdt == "f32" else "bf16"
+    wl = W.random_case(90 + D + window, seq_lens=[0, 1, 700, 2100, 33], num_q_heads=4,
+                       num_kv_heads=2, head_dim=D, block_size=16, q_dtype=qdt, kv_dtype=kvdt,
+                       sliding_window=window, partition_size=16)
+    kc, vc = oracle_caches(wl)
+    ref = oracle_decode(wl, kc, vc)
+    for k in kernels(kvdt, 2):
+        announce(f"reduce over many partitions {kvdt} D{D} window={window} kernel={k}")
+        with pa.decode_kernel(k):
+            dw = gpu_run(wl, split=True)
+        assert dw.max_parts == 132
+        assert_close(dw.out_f64(), ref, kvdt, f"many partitions ({k})")
+
+
 # ---------------------------------------------------------------------------
 # invariants on the device
 
