@@ -137,6 +137,9 @@ def main():
                     help="first run one plain device copy of this many MiB (a reference "
                          "kernel of known traffic for hardware-counter scaling)")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--cold-reps", type=int, default=30,
+                    help="calls timed one by one after a 1 GiB read+write flush of the caches "
+                         "(0: skip)")
     ap.add_argument("--kernel", choices=["auto", "valu", "mfma"], default="auto",
                     help="decode kernel family (auto: matrix cores for GQA groups >= 8)")
     args = ap.parse_args()
@@ -200,6 +203,34 @@ def main():
     torch.cuda.synchronize()
     T = time.perf_counter() - t0
 
+    cold = None
+    if args.cold_reps > 0:
+        # each call after a 1 GiB read+write pass that evicts L2 and the MALL
+        flush = torch.zeros((1 << 30) // 4, dtype=torch.float32, device="cuda")
+        dec_us, call_us = [], []
+        for _ in range(args.cold_reps):
+            flush.add_(1.0)
+            a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            a.record(stream)
+            if split:
+                dw.decode_split()
+            else:
+                dw.decode_unsplit()
+            b.record(stream)
+            if split:
+                dw.reduce()
+            c.record(stream)
+            torch.cuda.synchronize()
+            dec_us.append(a.elapsed_time(b) * 1e3)
+            call_us.append(a.elapsed_time(c) * 1e3)
+        del flush
+        pct = lambda v: {"p10": round(float(np.percentile(v, 10)), 2),
+                         "median": round(float(np.median(v)), 2),
+                         "p90": round(float(np.percentile(v, 90)), 2)}
+        cold = {"reps": args.cold_reps, "decode_us": pct(dec_us), "call_us": pct(call_us),
+                "decode_kv_GB/s_median": round(wl.kv_bytes() / (np.median(dec_us) * 1e-6) / 1e9, 1),
+                "flush": "1 GiB read+write before each call"}
+
     ms_step = T / args.steps * 1e3
     t_app = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
     t_dec = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
@@ -225,6 +256,8 @@ def main():
                               "reduce_lse": round(t_red, 2),
                               "wall_per_step": round(ms_step * 1e3, 2)},
         "kv_bytes_per_step": kv,
+        "unique_kv_bytes_per_step": int(wl.unique_kv_bytes()),
+        "cold": cold,
         "pct_of_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

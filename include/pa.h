@@ -207,8 +207,9 @@ const char* pa_decode_kernel_name(int kv_dtype, int num_q_heads, int num_kv_head
  * pa_probe_gather_read -- a measurement aid, not part of the attention path:
  * reads num_chunks chunks of chunk_bytes bytes, chunk k at
  * base + ids[k] * chunk_bytes, with the 16-byte non-temporal loads the decode
- * kernels use for K/V tiles, and XORs all the data into *sink (one device
- * word, not cleared).  With ids a random permutation it measures how fast HBM
+ * kernels use for K/V tiles (each chunk by one wave).  *sink (one device word)
+ * is written only when the XOR of a wave's data equals 0x9e3779b9, a store
+ * that keeps the loads from being dropped; callers need not read it.  With ids a random permutation it measures how fast HBM
  * serves a paged gather of tiles of that size; with ids in order, a streaming
  * read.  chunk_bytes: a power of two in [1024, 1 << 20]; base 16-byte aligned;
  * every ids[k] must address a chunk inside the caller's buffer (not checked).

@@ -123,7 +123,7 @@ int pa_decode(const void* query, const void* key_cache, const void* value_cache,
   p.partition_size = 0;
   p.max_parts = 1;
   return hip_status(pa::dispatch_decode(p, kv_dtype, head_dim, block_size,
-                                        num_q_heads / num_kv_heads, 1, (hipStream_t)stream));
+                                        num_q_heads / num_kv_heads, (hipStream_t)stream));
 }
 
 int pa_decode_split(const void* query, const void* key_cache, const void* value_cache,
@@ -152,8 +152,7 @@ int pa_decode_split(const void* query, const void* key_cache, const void* value_
   p.partition_size = partition_size;
   p.max_parts = max_num_partitions;
   return hip_status(pa::dispatch_decode(p, kv_dtype, head_dim, block_size,
-                                        num_q_heads / num_kv_heads, max_num_partitions,
-                                        (hipStream_t)stream));
+                                        num_q_heads / num_kv_heads, (hipStream_t)stream));
 }
 
 int pa_reduce_lse(const float* part_out, const float* part_lse, const int32_t* seq_lens,

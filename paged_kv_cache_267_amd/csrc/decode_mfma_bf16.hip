@@ -1,27 +1,27 @@
-// decode_mfma_bf16.hip -- instances of the matrix-core decode kernel for bf16 KV caches.
-#include "decode_mfma.h"
+// decode_mfma_bf16.hip -- matrix-core decode instances for bf16 KV caches.
+#include "decode_persistent.h"
 #include "dispatch.h"
+#include "tile_mfma.h"
 
 namespace pa {
 
 template <int D, int BS>
-static hipError_t by_group(const DecodeParams& p, int G, int parts, hipStream_t s) {
+static hipError_t by_group(const DecodeParams& p, int G, hipStream_t s) {
   switch (G) {
-    case 1: return launch_decode_mfma<KV_BF16, D, BS, 1>(p, parts, s);
-    case 2: return launch_decode_mfma<KV_BF16, D, BS, 2>(p, parts, s);
-    case 4: return launch_decode_mfma<KV_BF16, D, BS, 4>(p, parts, s);
-    case 8: return launch_decode_mfma<KV_BF16, D, BS, 8>(p, parts, s);
-    case 16: return launch_decode_mfma<KV_BF16, D, BS, 16>(p, parts, s);
+    case 1: return launch_decode_persistent<MfmaTile<KV_BF16, D, BS, 1>>(p, s);
+    case 2: return launch_decode_persistent<MfmaTile<KV_BF16, D, BS, 2>>(p, s);
+    case 4: return launch_decode_persistent<MfmaTile<KV_BF16, D, BS, 4>>(p, s);
+    case 8: return launch_decode_persistent<MfmaTile<KV_BF16, D, BS, 8>>(p, s);
+    case 16: return launch_decode_persistent<MfmaTile<KV_BF16, D, BS, 16>>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t decode_mfma_bf16(const DecodeParams& p, int D, int BS, int G, int parts,
-                           hipStream_t s) {
-  if (D == 64 && BS == 16) return by_group<64, 16>(p, G, parts, s);
-  if (D == 64 && BS == 32) return by_group<64, 32>(p, G, parts, s);
-  if (D == 128 && BS == 16) return by_group<128, 16>(p, G, parts, s);
-  if (D == 128 && BS == 32) return by_group<128, 32>(p, G, parts, s);
+hipError_t decode_mfma_bf16(const DecodeParams& p, int D, int BS, int G, hipStream_t s) {
+  if (D == 64 && BS == 16) return by_group<64, 16>(p, G, s);
+  if (D == 64 && BS == 32) return by_group<64, 32>(p, G, s);
+  if (D == 128 && BS == 16) return by_group<128, 16>(p, G, s);
+  if (D == 128 && BS == 32) return by_group<128, 32>(p, G, s);
   return hipErrorInvalidValue;
 }
 

@@ -1,79 +1,62 @@
-// decode_mfma.h -- paged decode attention on the gfx950 matrix cores, with a
-// persistent, balanced schedule.
+// decode_persistent.h -- paged decode attention on gfx950: the persistent,
+// balanced driver shared by the two tile computations (tile_mfma.h: both
+// contractions on the matrix cores; tile_valu.h: dot products on the VALU).
 //
 // Computation (sources: "vLLM 0.5 deep dive: PagedAttention architecture",
 // chenxutan.com, s2.2-s2.3; "vLLM 0.7.2 deep dive: PagedAttention v2 with
 // FlashAttention-3", jsqmd.com, s2.2-s2.3): per (sequence, query head), scaled
 // dot products of the query with every in-window key, gathered block by block
 // through the block table, a softmax kept stable by a running max and sum, and
-// the softmax-weighted sum of the values.  Both contractions of a 16-token
-// sub-tile run on MFMA:
-//   S^T = K . Q^T     v_mfma_f32_16x16x32_bf16: A = K (16 tokens x 32 dims, the
-//                     16-byte K groups exactly as they sit in the cache),
-//                     B = Q^T (32 dims x 16 heads; heads >= G are zero);
-//   O^T += V^T . P^T  v_mfma_f32_16x16x16_bf16: A = V^T (16 dims x 16 tokens,
-//                     4 consecutive tokens of one V row per lane), B = P^T.
-// Heads sit on the N axis, so lane l owns head l%16 in every fragment: the S^T
-// C-fragment is bit for bit the P^T B-fragment, and a head's running max, sum
-// and rescale are lane-local.  Per sub-tile the only cross-lane step is the
-// column max over the 4 lane rows (two permlane swaps).  The running max is
-// updated lazily: accumulators are rescaled only when a head's max grows by
-// more than 2^8, so p <= 256.  E4M3 codes are converted to bf16 in registers
-// (exact); k_scale is folded into the score scale, v_scale applied at the end.
+// the softmax-weighted sum of the values.  The unit of output is a segment:
+// one (sequence, KV head, partition) when split, one (sequence, KV head)
+// otherwise; its G query heads are served from one read of each K/V tile.
 //
-// Schedule.  A segment is one output unit: a partition (split) or a whole
-// sequence (unsplit).  The grid is sized to the resident capacity; workgroup w
-// serves KV head w % H_kv (workgroups are dealt to the 8 XCDs round-robin, so a
-// head stays on one XCD and a prefix shared by many sequences stays in its L2)
-// and takes that head's segments from one list, dealt to its J workgroups in
-// serpentine rounds: full partitions first (by sequence), then the partial ones
-// (a sequence's first or last partition, or the whole sequence when unsplit),
-// largest first.  Each workgroup builds the list from the lengths in LDS.
+// Schedule.  The grid is sized to the resident capacity; workgroup w serves KV
+// head w % H_kv (workgroups are dealt to the 8 XCDs round-robin, so a head
+// stays on one XCD and a prefix shared by many sequences stays in its L2) and
+// takes that head's segments from one list, dealt to its J workgroups in
+// serpentine rounds: full partitions first (by sequence), then the partial
+// ones (a sequence's first or last partition, or the whole sequence when
+// unsplit), largest first by a stable counting sort over size classes.  Each
+// workgroup builds the list from the lengths in LDS, so all agree on it.
 //
 // Memory pipeline.  The workgroup walks its segments in batches.  For a batch
 // it stages, in LDS, the block-table entries of every block the batch touches
-// and the query rows of its segments; after that the only global loads until
-// the batch ends are K/V sub-tiles.  Each wave streams its sub-tiles (the 4
-// waves take a segment's 16-token sub-tiles round-robin) two tiles ahead
+// and the query rows of its segments (blocks wholly before the window are
+// never listed); after that the only global loads until the batch ends are
+// K/V sub-tiles (16 tokens of one block).  Each wave streams its sub-tiles
+// (the 4 waves take a segment's sub-tiles round-robin) NBUF - 1 tiles ahead
 // across segment boundaries, with a fixed number of loads per step (a wave
 // past its last tile re-reads block 0), so every wait before a tile's first
-// use leaves the two younger tiles in flight.  At a segment end a wave
-// deposits its (max, sum, acc) in an LDS merge area and streams on; at its next
-// segment end (or after the batch's closing barrier) it merges a quarter of
-// that segment's output from the 4 deposits, in wave order, and writes it: the
-// output row (unsplit) or the partition's output and natural-log LSE (split).
-// Counters in LDS order deposits and merges, so no wave waits at a segment end
-// unless another wave is a whole segment behind.  A segment longer than the
-// staged table is carried into the next batch with its running state.
+// use leaves the younger tiles in flight.
+//
+// Merge.  At a segment end a wave deposits its (max, sum, acc) in an LDS merge
+// area and streams on; at its next segment end (or after the batch's closing
+// barrier) it merges a quarter of that segment's output from the 4 deposits,
+// in wave order, and writes it: the output row (unsplit) or the partition's
+// output and natural-log LSE (split).  Counters in LDS order deposits and
+// merges, so no wave waits at a segment end unless another wave is a whole
+// segment behind.  A segment longer than the staged table is carried into the
+// next batch with its running state.
+//
+// Tile policy interface (T): constants KV, D, BS, G, E (KV element bytes), EQ
+// (query element bytes), OUT_F32, NBUF, QROWB (staged query row bytes), QBYTES
+// (LDS for staged queries), NPAR (merge areas); types Buf (one sub-tile in
+// registers, with fields slot and st) and WaveLds (per-wave LDS scratch); and
+// the device members reset(), load(Buf&, k_tile, v_tile, sub),
+// set_query(staged rows), compute(Buf&, t0, t1, qk_scale, WaveLds&) and
+// deposit(m[G], l[G], acc[G][D + 4]).
 #pragma once
 
 #include "common.h"
 
 namespace pa {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-
-constexpr int MFMA_WAVES = 4;
-constexpr int MFMA_SEQ_CHUNK = 1024;   // sequences per launch (schedule kept in LDS)
-constexpr int MFMA_TBL = 2048;         // block-table entries staged per batch
-constexpr float LAZY_RESCALE_LOG2 = 8.0f;
-// register buffers per wave: NBUF - 1 sub-tiles in flight while one is
-// computed (E4M3 sub-tiles are half the bytes, so twice as many)
-template <int KV> struct MfmaDepth { static constexpr int NBUF = KV == KV_FP8 ? 5 : 3; };
-// query operand: kept in registers per segment (true) or read from LDS per tile
-constexpr bool MFMA_QREG = true;
-
-template <int D, int G>
-struct MfmaGeom {
-  static constexpr int QROW = D + 8;                       // padded query row (elements)
-  static constexpr int QBYTES = G <= 8 ? 16384 : 8192;     // LDS for staged queries
-  static constexpr int SLOTS_RAW = QBYTES / (G * QROW * 2);
-  static constexpr int SLOTS = SLOTS_RAW < 32 ? SLOTS_RAW : 32;  // segments per batch
-  // merge areas, used by successive segment ends in turn: two when they fit
-  // (then a wave never waits at a segment end), else one
-  static constexpr int NPAR = G <= 8 ? 2 : 1;
-};
+constexpr int PD_WAVES = 4;
+constexpr int PD_SEQ_CHUNK = 1024;    // sequences per launch (schedule kept in LDS)
+constexpr int PD_TBL = 2048;          // block-table entries staged per batch
+constexpr int PD_SORT_MAX = 512;      // partial segments ordered by size (more: by sequence)
+constexpr int PD_SIZE_CLASSES = 64;   // size classes of that order (one per lane of a wave)
 
 // Per-batch description of one segment slot.
 struct SegMeta {
@@ -86,66 +69,53 @@ struct SegMeta {
   int fin;      // the segment ends in this batch
 };
 
-constexpr int MFMA_SORT_MAX = 512;     // partial segments ordered by size (more: by sequence)
-constexpr int MFMA_SIZE_CLASSES = 64;  // size classes of that order (one per lane of a wave)
+template <class T>
+struct PdGeom {
+  static constexpr int SLOTS_RAW = T::QBYTES / (T::G * T::QROWB);
+  static constexpr int SLOTS = SLOTS_RAW < 32 ? SLOTS_RAW : 32;  // segments per batch
+  static_assert(SLOTS >= 1, "query staging too small");
+};
 
-template <int D, int G>
-struct MfmaSmem {
-  int32_t lens[MFMA_SEQ_CHUNK];        // clamped lengths
-  int32_t fpre[MFMA_SEQ_CHUNK + 1];    // full partitions before each sequence (exclusive)
-  int32_t ppre[MFMA_SEQ_CHUNK + 1];    // partial segments before each sequence (exclusive)
-  alignas(16) int32_t plist[MFMA_SORT_MAX];  // partial segments, largest first: (s << 20) | p
-  int32_t tbl[MFMA_TBL];               // staged block ids of the batch
-  uint16_t q[MfmaGeom<D, G>::SLOTS][G][MfmaGeom<D, G>::QROW];
-  SegMeta meta[MfmaGeom<D, G>::SLOTS];
-  int32_t bcount, bnext_m, bnext_st, scan[2][MFMA_WAVES];
-  int32_t arrived[MfmaGeom<D, G>::NPAR];  // deposits into each area (4 per use)
-  int32_t done[MfmaGeom<D, G>::NPAR];     // quarter merges out of each area (4 per use)
+template <class T>
+struct PdSmem {
+  static constexpr int G = T::G, D = T::D, SLOTS = PdGeom<T>::SLOTS;
+  int32_t lens[PD_SEQ_CHUNK];        // clamped lengths
+  int32_t fpre[PD_SEQ_CHUNK + 1];    // full partitions before each sequence (exclusive)
+  int32_t ppre[PD_SEQ_CHUNK + 1];    // partial segments before each sequence (exclusive)
+  alignas(16) int32_t plist[PD_SORT_MAX];  // partial segments, largest first: (s << 20) | p
+  int32_t tbl[PD_TBL];               // staged block ids of the batch
+  alignas(16) uint8_t q[SLOTS][G][T::QROWB];   // staged query rows of the batch
+  SegMeta meta[SLOTS];
+  int32_t bcount, bnext_m, bnext_st, scan[2][PD_WAVES];
+  int32_t arrived[T::NPAR];          // deposits into each merge area (4 per use)
+  int32_t done[T::NPAR];             // quarter merges out of each area (4 per use)
+  typename T::WaveLds wl[PD_WAVES];  // per-wave scratch of the tile computation
   union alignas(16) {
     struct {
-      float m[MFMA_WAVES][G];
-      float l[MFMA_WAVES][G];
-      float acc[MFMA_WAVES][G][D + 4];    // rows padded: no bank conflicts
-    } area[MfmaGeom<D, G>::NPAR];
-    struct {                              // ordering of the partial segments, before any merge
-      int32_t cls[MFMA_SORT_MAX];
-      int32_t cnt[MFMA_SORT_MAX / 64][MFMA_SIZE_CLASSES];
+      float m[PD_WAVES][G];
+      float l[PD_WAVES][G];
+      float acc[PD_WAVES][G][D + 4];  // rows padded: no bank conflicts
+    } area[T::NPAR];
+    struct {                          // ordering of the partial segments, before any merge
+      int32_t cls[PD_SORT_MAX];
+      int32_t cnt[PD_SORT_MAX / 64][PD_SIZE_CLASSES];
     } srt;
   } u;
 };
 
-__device__ __forceinline__ float colmax4(float x) {
-  // max over the 4 lane rows of a column (lanes l, l^16, l^32, l^48)
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float colsum4(float x) {
-  const float y = swap_add32(x, x);
-  return swap_add16(y, y);
-}
-
-template <int KV, int D, int BS, int G>
-__global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodeParams p) {
-  static_assert(KV == KV_BF16 || KV == KV_FP8, "matrix path takes bf16 or E4M3 caches");
-  static_assert(G <= 16, "at most 16 query heads per KV head");
-  using Geo = MfmaGeom<D, G>;
-  constexpr int E = KvTraits<KV>::E;
-  constexpr int KS = D / 32;          // QK k-steps of 32 dims
-  constexpr int NB = D / 16;          // PV n-blocks of 16 dims
-  constexpr int KL = D * E / 64;      // 16-byte K loads per lane per sub-tile
-  constexpr int VW = E;               // V dwords per lane per n-block (bf16: 2, fp8: 1)
+template <class T>
+__global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(DecodeParams p) {
+  constexpr int D = T::D, BS = T::BS, G = T::G, E = T::E, EQ = T::EQ;
   constexpr int SPB = BS / 16;
   constexpr size_t TILE_BYTES = (size_t)D * BS * E;
-  constexpr int NTH = 64 * MFMA_WAVES;
-  constexpr int SLOTS = Geo::SLOTS;
-  static_assert(SLOTS >= 1, "query staging too small");
+  constexpr int NTH = 64 * PD_WAVES;
+  constexpr int SLOTS = PdGeom<T>::SLOTS;
+  constexpr int NPAR = T::NPAR;
+  static_assert(G <= 16, "at most 16 query heads per KV head");
 
-  __shared__ MfmaSmem<D, G> sm;
+  __shared__ PdSmem<T> sm;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int row = lane >> 4, col = lane & 15;
   const int H = p.num_kv_heads, Hq = p.num_q_heads;
   const int hk = blockIdx.x % H;
   const int j = blockIdx.x / H, J = gridDim.x / H;
@@ -208,12 +178,13 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
     __syncthreads();
   }
   const int F = uniform(sm.fpre[S]), NPART = uniform(sm.ppre[S]);
-  const bool sorted = NPART <= MFMA_SORT_MAX;
+  const bool sorted = NPART <= PD_SORT_MAX;
   if (sorted) {
     // list the partial segments with a size class (4 classes per octave;
     // larger segments get smaller classes), then order them by class with a
     // stable counting sort, so every workgroup derives the same order
-    constexpr int NBK = MFMA_SIZE_CLASSES, CHUNKS = MFMA_SORT_MAX / 64, SR = MFMA_SORT_MAX / NTH;
+    constexpr int NBK = PD_SIZE_CLASSES, CHUNKS = PD_SORT_MAX / 64, SR = PD_SORT_MAX / NTH;
+    static_assert(NBK == 64, "one size class per lane");
     auto size_class = [](int sz) -> int {
       if (sz <= 0) return NBK - 1;
       const int lz = 31 - __builtin_clz(sz);
@@ -285,7 +256,7 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
         sm.plist[sm.u.srt.cnt[wave + r * (NTH / 64)][cls[r]] + wr[r]] = mine[r];
     __syncthreads();
   }
-  if (tid < MfmaGeom<D, G>::NPAR) {
+  if (tid < NPAR) {
     sm.arrived[tid] = 0;
     sm.done[tid] = 0;
   }
@@ -338,32 +309,12 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
   const size_t block_stride = (size_t)H * TILE_BYTES;
   const unsigned nb_max = (unsigned)(p.num_blocks - 1);
 
-  // lane offsets inside a sub-tile
-  const uint32_t koff0 = (uint32_t)((row * BS + col) * 16);
-  const uint32_t voff0 = (uint32_t)((col * BS + 4 * row) * E);
-
-  struct Buf {
-    uint4 k[KL];
-    uint32_t v[NB][VW];
-    int slot;   // segment slot in the batch (-1: no tile)
-    int st;     // sub-tile index
-  };
-  Buf bufs[MfmaDepth<KV>::NBUF];
-
+  using Buf = typename T::Buf;
+  Buf bufs[T::NBUF];
   // running state of the segment being computed (carried across batches when a
   // segment continues)
-  f32x4_t acc[NB];
-  float m_ref = -INFINITY, l_run = 0.f;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  bf16x8_t qop[KS];
-
-  auto reset = [&]() {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    m_ref = -INFINITY;
-    l_run = 0.f;
-  };
+  T tile;
+  tile.reset();
 
   // segment ends this wave has passed (the same sequence in every wave), and
   // the last one, whose quarter merge is still to do (pend_s < 0: none)
@@ -379,9 +330,9 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
   // segment's G x D block.
   auto merge_quarter = [&]() {
     if (pend_s < 0) return;
-    constexpr int QN = G * D / MFMA_WAVES;
+    constexpr int QN = G * D / PD_WAVES;
     const int par = pend_par;
-    spin_until(&sm.arrived[par], MFMA_WAVES * (pend_gen + 1));
+    spin_until(&sm.arrived[par], PD_WAVES * (pend_gen + 1));
     auto& ar = sm.u.area[par];
 #pragma unroll
     for (int i0 = 0; i0 < QN; i0 += 64) {
@@ -390,10 +341,10 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
         const int g = e / D, d = e % D;
         float mx = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < MFMA_WAVES; ++w) mx = fmaxf(mx, ar.m[w][g]);
+        for (int w = 0; w < PD_WAVES; ++w) mx = fmaxf(mx, ar.m[w][g]);
         float den = 0.f, num = 0.f;
 #pragma unroll
-        for (int w = 0; w < MFMA_WAVES; ++w) {
+        for (int w = 0; w < PD_WAVES; ++w) {
           const float f =
               (mx == -INFINITY || ar.m[w][g] == -INFINITY) ? 0.f : fast_exp2(ar.m[w][g] - mx);
           den += f * ar.l[w][g];
@@ -402,7 +353,8 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
         const float o = den > 0.f ? num * (p.v_scale / den) : 0.f;
         const size_t r = (size_t)pend_s * Hq + hk * G + g;
         if (p.part_out == nullptr) {
-          ((uint16_t*)p.out)[r * D + d] = to_bf16_bits(o);
+          if (T::OUT_F32) ((float*)p.out)[r * D + d] = o;
+          else ((uint16_t*)p.out)[r * D + d] = to_bf16_bits(o);
         } else {
           const size_t pi = r * p.max_parts + pend_pp;
           p.part_out[pi * D + d] = o;
@@ -434,7 +386,7 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
         // [a / SPB, ceil(b / SPB)); a segment that does not fit starts a new batch,
         // unless it is the first slot (then it takes what fits and continues)
         int b = st_hi;
-        const int room = MFMA_TBL - used;
+        const int room = PD_TBL - used;
         if (b > a && (b + SPB - 1) / SPB - a / SPB > room) {
           if (cnt > 0) { next_m = m; next_st = st_start; break; }
           b = (a / SPB + room) * SPB;
@@ -474,9 +426,11 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
         const unsigned id = (unsigned)trow[i];
         sm.tbl[t + i] = (int)(id > nb_max ? nb_max : id);
       }
-      const uint16_t* qsrc = (const uint16_t*)p.q + ((size_t)(s0 + si) * Hq + hk * G) * D;
-      for (int i = tid; i < G * D / 8; i += NTH)
-        *(uint4*)&sm.q[c][(i * 8) / D][(i * 8) % D] = *(const uint4*)(qsrc + i * 8);
+      // G query rows of D * EQ bytes, 16 bytes per thread step
+      constexpr int QV = D * EQ / 16;
+      const uint8_t* qsrc = (const uint8_t*)p.q + ((size_t)(s0 + si) * Hq + hk * G) * D * EQ;
+      for (int i = tid; i < G * QV; i += NTH)
+        *(uint4*)&sm.q[c][i / QV][(i % QV) * 16] = *(const uint4*)(qsrc + (size_t)i * 16);
     }
     __syncthreads();
 
@@ -485,9 +439,8 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
     // sub-tile; first_st(c) is this wave's first sub-tile >= st_a in slot c.
     auto first_st = [&](int c) -> int {
       const int st_lo = uniform(sm.meta[c].t0) >> 4, a = uniform(sm.meta[c].st_a);
-      return a + (((wave - (a - st_lo)) % MFMA_WAVES) + MFMA_WAVES) % MFMA_WAVES;
+      return a + (((wave - (a - st_lo)) % PD_WAVES) + PD_WAVES) % PD_WAVES;
     };
-    auto next_st = [&](int st) -> int { return st + MFMA_WAVES; };
     int cs = 0, cst = nslot > 0 ? first_st(0) : 0;   // load cursor: slot, sub-tile
     auto settle = [&]() {        // move the cursor to a slot with a tile left
       while (cs < nslot && cst >= uniform(sm.meta[cs].st_b)) {
@@ -505,125 +458,16 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
         phys = uniform(sm.tbl[uniform(sm.meta[cs].tbl) + blk]);
         b.slot = cs;
         b.st = st;
-        cst = next_st(cst);
+        cst += PD_WAVES;
         settle();
       } else {
         b.slot = -1;             // past the end: re-read block 0 (keeps the load count fixed)
         b.st = 0;
       }
-      const int sub = st % SPB;
-      const char* kp = kbase + (size_t)phys * block_stride + sub * 256 + koff0;
-      const char* vp = vbase + (size_t)phys * block_stride + sub * 16 * E + voff0;
-#pragma unroll
-      for (int i = 0; i < KL; ++i) b.k[i] = load_nt16(kp + i * 4 * BS * 16);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const char* a = vp + (size_t)nb * 16 * BS * E;
-        // a 32-token block's V row is shared by its two sub-tiles, which run on
-        // different waves: ordinary loads keep the line in L2 for the other
-        // half; 16-token rows are used whole and stream past L2
-        if (VW == 2) {
-          const u32x2_t t = SPB == 1 ? __builtin_nontemporal_load((const u32x2_t*)a)
-                                     : *(const u32x2_t*)a;
-          b.v[nb][0] = t.x;
-          b.v[nb][VW - 1] = t.y;
-        } else {
-          b.v[nb][0] = SPB == 1 ? __builtin_nontemporal_load((const uint32_t*)a)
-                                : *(const uint32_t*)a;
-        }
-      }
+      tile.load(b, kbase + (size_t)phys * block_stride, vbase + (size_t)phys * block_stride,
+                st % SPB);
     };
-
-    auto q_to_regs = [&](int c) {
-      if (!MFMA_QREG) return;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int d0 = (KV == KV_BF16) ? 32 * ks + 8 * row : 16 * (row + 4 * (ks >> 1)) + 8 * (ks & 1);
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (col < G) v = *(const uint4*)&sm.q[c][col][d0];
-        qop[ks] = __builtin_bit_cast(bf16x8_t, (u32x4_t){v.x, v.y, v.z, v.w});
-      }
-    };
-
-    auto compute_tile = [&](Buf& b) {
-      if (!MFMA_QREG) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int d0 =
-              (KV == KV_BF16) ? 32 * ks + 8 * row : 16 * (row + 4 * (ks >> 1)) + 8 * (ks & 1);
-          uint4 v = make_uint4(0, 0, 0, 0);
-          if (col < G) v = *(const uint4*)&sm.q[b.slot][col][d0];
-          qop[ks] = __builtin_bit_cast(bf16x8_t, (u32x4_t){v.x, v.y, v.z, v.w});
-        }
-      }
-      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < KL; ++i) {
-        if (KV == KV_BF16) {
-          const bf16x8_t kop =
-              __builtin_bit_cast(bf16x8_t, (u32x4_t){b.k[i].x, b.k[i].y, b.k[i].z, b.k[i].w});
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[i], sacc, 0, 0, 0);
-        } else {
-          const u32x4_t lo4 = {fp8x2_to_bf16x2<false>(b.k[i].x), fp8x2_to_bf16x2<true>(b.k[i].x),
-                               fp8x2_to_bf16x2<false>(b.k[i].y), fp8x2_to_bf16x2<true>(b.k[i].y)};
-          const u32x4_t hi4 = {fp8x2_to_bf16x2<false>(b.k[i].z), fp8x2_to_bf16x2<true>(b.k[i].z),
-                               fp8x2_to_bf16x2<false>(b.k[i].w), fp8x2_to_bf16x2<true>(b.k[i].w)};
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo4),
-                                                         qop[2 * i], sacc, 0, 0, 0);
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi4),
-                                                         qop[2 * i + 1], sacc, 0, 0, 0);
-        }
-      }
-      float sc[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) sc[jj] = sacc[jj] * p.qk_scale;
-
-      const int st = b.st;
-      const int t0 = uniform(sm.meta[b.slot].t0), t1 = uniform(sm.meta[b.slot].t1);
-      if ((st * 16 < t0) || (st * 16 + 16 > t1)) {  // partial sub-tile: mask scores, zero V
-        uint32_t vmask[VW];
-#pragma unroll
-        for (int w = 0; w < VW; ++w) vmask[w] = 0u;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int tok = st * 16 + 4 * row + jj;
-          const bool ok = tok >= t0 && tok < t1;
-          if (!ok) sc[jj] = -INFINITY;
-          if (ok) {
-            if (KV == KV_BF16) vmask[jj >> 1] |= 0xffffu << (16 * (jj & 1));
-            else vmask[0] |= 0xffu << (8 * jj);
-          }
-        }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int w = 0; w < VW; ++w) b.v[nb][w] &= vmask[w];
-      }
-
-      const float cmax = colmax4(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-      if (__builtin_amdgcn_ballot_w64(cmax > m_ref + LAZY_RESCALE_LOG2) != 0) {
-        const float m_new = fmaxf(m_ref, cmax);
-        const float alpha = fast_exp2(m_ref - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
-        m_ref = m_new;
-      }
-      float pr[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) pr[jj] = fast_exp2(sc[jj] - m_ref);
-      l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-      const s16x4_t pop = __builtin_bit_cast(
-          s16x4_t, (u32x2_t){pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        u32x2_t vv;
-        if (KV == KV_BF16) vv = (u32x2_t){b.v[nb][0], b.v[nb][VW - 1]};
-        else vv = (u32x2_t){fp8x2_to_bf16x2<false>(b.v[nb][0]), fp8x2_to_bf16x2<true>(b.v[nb][0])};
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, vv), pop,
-                                                           acc[nb], 0, 0, 0);
-      }
-    };
+    auto set_query = [&](int c) { tile.set_query(&sm.q[c][0][0]); };
 
     // ---- segment ends (slots with fin = 1) ------------------------------------------------
     // A wave first does its quarter of the previous segment's merge (all waves
@@ -632,24 +476,15 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
     // waits for another unless it is a whole segment ahead.
     auto finish_slot = [&](int c) {
       if (!uniform(sm.meta[c].fin)) return;  // continues in the next batch
-      constexpr int NPAR = MfmaGeom<D, G>::NPAR;
       merge_quarter();
       const int par = uses % NPAR, gen = uses / NPAR;
       ++uses;
-      spin_until(&sm.done[par], MFMA_WAVES * gen);   // the area's previous use is merged
+      spin_until(&sm.done[par], PD_WAVES * gen);   // the area's previous use is merged
       auto& ar = sm.u.area[par];
-      const float l_col = colsum4(l_run);
-      if (col < G) {
-        if (row == 0) {
-          ar.m[wave][col] = m_ref;
-          ar.l[wave][col] = l_col;
-        }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) *(f32x4_t*)&ar.acc[wave][col][16 * nb + 4 * row] = acc[nb];
-      }
+      tile.deposit(ar.m[wave], ar.l[wave], ar.acc[wave]);
       if (lane == 0)
         __hip_atomic_fetch_add(&sm.arrived[par], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      reset();
+      tile.reset();
       pend_s = s0 + uniform(sm.meta[c].s);
       pend_pp = uniform(sm.meta[c].p);
       pend_par = par;
@@ -657,9 +492,9 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
     };
 
     // ---- main loop: NBUF buffers, NBUF - 1 tiles in flight --------------------------------
-    constexpr int NBUF = MfmaDepth<KV>::NBUF;
+    constexpr int NBUF = T::NBUF;
     int cur = 0;                 // slot whose state the wave holds
-    q_to_regs(0);
+    set_query(0);
 #pragma unroll
     for (int i = 0; i + 1 < NBUF; ++i) load_tile(bufs[i]);
     auto step = [&](Buf& cb, Buf& spare) -> bool {
@@ -668,10 +503,11 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
       while (cur < target) {     // every slot is visited, in order, by every wave
         finish_slot(cur);
         ++cur;
-        if (cur < nslot) q_to_regs(cur);
+        if (cur < nslot) set_query(cur);
       }
       if (cb.slot < 0) return false;
-      compute_tile(cb);
+      tile.compute(cb, uniform(sm.meta[cb.slot].t0), uniform(sm.meta[cb.slot].t1), p.qk_scale,
+                   sm.wl[wave]);
       return true;
     };
     // the loop is left only through the exits, so every trip through the body
@@ -687,15 +523,15 @@ __global__ __launch_bounds__(64 * MFMA_WAVES) void decode_mfma_kernel(DecodePara
   }
 }
 
-// Grid: resident capacity, a multiple of num_kv_heads.
-template <int KV, int D, int BS, int G>
-hipError_t launch_decode_mfma(const DecodeParams& p0, int parts, hipStream_t stream) {
-  (void)parts;
+// Grid: resident capacity, a multiple of num_kv_heads; sequences in launches
+// of PD_SEQ_CHUNK.
+template <class T>
+hipError_t launch_decode_persistent(const DecodeParams& p0, hipStream_t stream) {
   static int per_cu = -1;
   if (per_cu < 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<KV, D, BS, G>,
-                                                     64 * MFMA_WAVES, 0) != hipSuccess || n < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_persistent_kernel<T>,
+                                                     64 * PD_WAVES, 0) != hipSuccess || n < 1)
       n = 1;
     per_cu = n;
   }
@@ -705,15 +541,15 @@ hipError_t launch_decode_mfma(const DecodeParams& p0, int parts, hipStream_t str
     cus = 256;
   const int H = p0.num_kv_heads;
   DecodeParams p = p0;
-  for (int s0 = 0; s0 < p0.num_seqs; s0 += MFMA_SEQ_CHUNK) {
+  for (int s0 = 0; s0 < p0.num_seqs; s0 += PD_SEQ_CHUNK) {
     p.seq_begin = s0;
-    p.seq_count = min(MFMA_SEQ_CHUNK, p0.num_seqs - s0);
+    p.seq_count = min(PD_SEQ_CHUNK, p0.num_seqs - s0);
     const long long work = (long long)p.seq_count * (p.partition_size > 0 ? p.max_parts : 1);
     long long J = ((long long)cus * per_cu + H - 1) / H;
     if (J > work) J = work;
     if (J < 1) J = 1;
-    hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, G>), dim3((unsigned)(J * H)),
-                       dim3(64 * MFMA_WAVES), 0, stream, p);
+    hipLaunchKernelGGL((decode_persistent_kernel<T>), dim3((unsigned)(J * H)),
+                       dim3(64 * PD_WAVES), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

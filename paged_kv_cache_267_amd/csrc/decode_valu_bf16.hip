@@ -1,26 +1,26 @@
-// decode_valu_bf16.hip -- instances of the VALU decode kernel for bf16 KV caches.
-#include "decode_valu.h"
+// decode_valu_bf16.hip -- vector-ALU decode instances for bf16 KV caches.
+#include "decode_persistent.h"
 #include "dispatch.h"
+#include "tile_valu.h"
 
 namespace pa {
 
 template <int D, int BS>
-static hipError_t by_group(const DecodeParams& p, int G, int parts, int waves, hipStream_t s) {
+static hipError_t by_group(const DecodeParams& p, int G, hipStream_t s) {
   switch (G) {
-    case 1: return launch_decode_valu<KV_BF16, D, BS, 1>(p, parts, waves, s);
-    case 2: return launch_decode_valu<KV_BF16, D, BS, 2>(p, parts, waves, s);
-    case 4: return launch_decode_valu<KV_BF16, D, BS, 4>(p, parts, waves, s);
-    case 8: return launch_decode_valu<KV_BF16, D, BS, 8>(p, parts, waves, s);
+    case 1: return launch_decode_persistent<ValuTile<KV_BF16, D, BS, 1>>(p, s);
+    case 2: return launch_decode_persistent<ValuTile<KV_BF16, D, BS, 2>>(p, s);
+    case 4: return launch_decode_persistent<ValuTile<KV_BF16, D, BS, 4>>(p, s);
+    case 8: return launch_decode_persistent<ValuTile<KV_BF16, D, BS, 8>>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t decode_valu_bf16(const DecodeParams& p, int D, int BS, int G, int parts, int waves,
-                           hipStream_t s) {
-  if (D == 64 && BS == 16) return by_group<64, 16>(p, G, parts, waves, s);
-  if (D == 64 && BS == 32) return by_group<64, 32>(p, G, parts, waves, s);
-  if (D == 128 && BS == 16) return by_group<128, 16>(p, G, parts, waves, s);
-  if (D == 128 && BS == 32) return by_group<128, 32>(p, G, parts, waves, s);
+hipError_t decode_valu_bf16(const DecodeParams& p, int D, int BS, int G, hipStream_t s) {
+  if (D == 64 && BS == 16) return by_group<64, 16>(p, G, s);
+  if (D == 64 && BS == 32) return by_group<64, 32>(p, G, s);
+  if (D == 128 && BS == 16) return by_group<128, 16>(p, G, s);
+  if (D == 128 && BS == 32) return by_group<128, 32>(p, G, s);
   return hipErrorInvalidValue;
 }
 

@@ -29,17 +29,16 @@ bool decode_uses_mfma(int kv_dtype, int G) {
   }
 }
 
-hipError_t dispatch_decode(const DecodeParams& p, int kv_dtype, int D, int BS, int G, int parts,
+hipError_t dispatch_decode(const DecodeParams& p, int kv_dtype, int D, int BS, int G,
                            hipStream_t stream) {
-  const int waves = VALU_WAVES;
   if (decode_uses_mfma(kv_dtype, G)) {
-    if (kv_dtype == PA_BF16) return decode_mfma_bf16(p, D, BS, G, parts, stream);
-    return decode_mfma_fp8(p, D, BS, G, parts, stream);
+    if (kv_dtype == PA_BF16) return decode_mfma_bf16(p, D, BS, G, stream);
+    return decode_mfma_fp8(p, D, BS, G, stream);
   }
   switch (kv_dtype) {
-    case PA_F32: return decode_valu_f32(p, D, BS, G, parts, waves, stream);
-    case PA_BF16: return decode_valu_bf16(p, D, BS, G, parts, waves, stream);
-    case PA_FP8_E4M3: return decode_valu_fp8(p, D, BS, G, parts, waves, stream);
+    case PA_F32: return decode_valu_f32(p, D, BS, G, stream);
+    case PA_BF16: return decode_valu_bf16(p, D, BS, G, stream);
+    case PA_FP8_E4M3: return decode_valu_fp8(p, D, BS, G, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -7,24 +7,16 @@
 
 namespace pa {
 
-// Waves per workgroup of the VALU decode kernel.
-constexpr int VALU_WAVES = 4;
-
-// VALU (bandwidth) path, one function per KV element type; they switch over
-// (head_dim, block_size, group) and return hipErrorInvalidValue for a
-// combination that is not instantiated.
-hipError_t decode_valu_f32(const DecodeParams& p, int D, int BS, int G, int parts, int waves,
-                           hipStream_t stream);
-hipError_t decode_valu_bf16(const DecodeParams& p, int D, int BS, int G, int parts, int waves,
-                            hipStream_t stream);
-hipError_t decode_valu_fp8(const DecodeParams& p, int D, int BS, int G, int parts, int waves,
-                           hipStream_t stream);
-
-// Matrix-core path (bf16 / E4M3 caches, G in {1, 2, 4, 8, 16}).
-hipError_t decode_mfma_bf16(const DecodeParams& p, int D, int BS, int G, int parts,
-                            hipStream_t stream);
-hipError_t decode_mfma_fp8(const DecodeParams& p, int D, int BS, int G, int parts,
-                           hipStream_t stream);
+// Decode instances on the persistent driver (decode_persistent.h), one function
+// per (tile computation, KV element type); they switch over (head_dim,
+// block_size, group) and return hipErrorInvalidValue for a combination that is
+// not instantiated.  Vector-ALU tiles: G in {1, 2, 4, 8}; matrix-core tiles
+// (bf16 / E4M3 caches): G in {1, 2, 4, 8, 16}.
+hipError_t decode_valu_f32(const DecodeParams& p, int D, int BS, int G, hipStream_t stream);
+hipError_t decode_valu_bf16(const DecodeParams& p, int D, int BS, int G, hipStream_t stream);
+hipError_t decode_valu_fp8(const DecodeParams& p, int D, int BS, int G, hipStream_t stream);
+hipError_t decode_mfma_bf16(const DecodeParams& p, int D, int BS, int G, hipStream_t stream);
+hipError_t decode_mfma_fp8(const DecodeParams& p, int D, int BS, int G, hipStream_t stream);
 
 // Process-wide kernel-family choice (pa_kernel_choice); set returns -1 for an
 // unknown value.
@@ -35,9 +27,8 @@ int get_decode_kernel();
 // current choice.
 bool decode_uses_mfma(int kv_dtype, int G);
 
-// Chooses the kernel family for (KV dtype, group size) and launches it with a
-// grid of (num_kv_heads, parts, num_seqs).
-hipError_t dispatch_decode(const DecodeParams& p, int kv_dtype, int D, int BS, int G, int parts,
+// Chooses the tile computation for (KV dtype, group size) and launches it.
+hipError_t dispatch_decode(const DecodeParams& p, int kv_dtype, int D, int BS, int G,
                            hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc, void* vc,
