@@ -74,6 +74,45 @@ def load_traffic(kernel_hash: str, workload: str, mode: str):
     return r.get("bytes_per_launch")
 
 
+def record_traffic(fetch_csv: str, write_csv: str, key: str, khash: str, copy_mib: int) -> dict:
+    """HBM bytes per launch of the decode kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled so that the
+    plain device copy of copy_mib MiB in the same run reads / writes exactly
+    its size.  Merged into profiles/decode_traffic.json under key."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    pick = lambda d, s: [v for k, vs in d.items() if s in k for v in vs]
+    copy_kib = copy_mib * 1024.0
+    sf = copy_kib / max(pick(f, "copyBuffer"))
+    sw = copy_kib / max(pick(w, "copyBuffer"))
+    df, dwr = pick(f, "decode_persistent_kernel"), pick(w, "decode_persistent_kernel")
+    fb = statistics.mean(df) * 1024 * sf
+    wb = statistics.mean(dwr) * 1024 * sw
+    rec = {"kernel_hash": khash, "bytes_per_launch": int(fb + wb), "fetch_bytes": int(fb),
+           "write_bytes": int(wb), "fetch_scale": round(sf, 4), "write_scale": round(sw, 4),
+           "dispatches": [len(df), len(dwr)],
+           "source": "rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of bench.py"}
+    try:
+        allrec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        allrec = {}
+    allrec[key] = rec
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(allrec, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    return rec
+
+
 def read_ceiling(chunk_bytes: int, gib: int = 2, reps: int = 10):
     """What HBM delivers to this access pattern on this GPU: the library's
     gather-read probe over a fresh 2 GiB buffer cut into chunks of one
@@ -137,6 +176,10 @@ def main():
                     help="first run one plain device copy of this many MiB (a reference "
                          "kernel of known traffic for hardware-counter scaling)")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: store the decode kernel's HBM bytes per launch from "
+                         "rocprofv3 counter CSVs of this configuration (with "
+                         "--calibrate-copy-mib set as in those runs)")
     ap.add_argument("--cold-reps", type=int, default=30,
                     help="calls timed one by one after a 1 GiB read+write flush of the caches "
                          "(0: skip)")
@@ -155,13 +198,21 @@ def main():
     from paged_kv_cache_267_amd import workloads as W
     from paged_kv_cache_267_amd.harness import DeviceWorkload
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = W.config(args.config)
     pa.pa_set_decode_kernel(args.kernel)
     kv_code = {"f32": pa.PA_F32, "bf16": pa.PA_BF16, "fp8_e4m3": pa.PA_FP8_E4M3}[wl.kv_dtype]
     kernel = pa.pa_decode_kernel_name(kv_code, wl.num_q_heads, wl.num_kv_heads)
     split = args.mode == "split"
     psize = args.partition_size or wl.partition_size
+    khash = kernel_source_hash()
+    mode_key = f"{kernel}/{args.mode}{psize if split else ''}"
+    if args.record_traffic:
+        assert args.calibrate_copy_mib > 0, "--calibrate-copy-mib must name the copy size"
+        rec = record_traffic(*args.record_traffic, f"{wl.name}/{mode_key}", khash,
+                             args.calibrate_copy_mib)
+        print(json.dumps({f"{wl.name}/{mode_key}": rec}))
+        return
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
     dw = DeviceWorkload(wl, partition_size=psize)
     dw.fill_history()
     torch.cuda.synchronize()
@@ -205,11 +256,15 @@ def main():
 
     cold = None
     if args.cold_reps > 0:
-        # each call after a 1 GiB read+write pass that evicts L2 and the MALL
+        # each call after a 1 GiB read+write pass that evicts L2 and the MALL,
+        # then a 512 MiB read of another buffer that writes the dirty lines back
+        # (so no write-back of the flush overlaps the timed call)
         flush = torch.zeros((1 << 30) // 4, dtype=torch.float32, device="cuda")
+        clean = torch.zeros((512 << 20) // 4, dtype=torch.float32, device="cuda")
         dec_us, call_us = [], []
         for _ in range(args.cold_reps):
             flush.add_(1.0)
+            clean.sum()
             a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
             a.record(stream)
             if split:
@@ -223,13 +278,13 @@ def main():
             torch.cuda.synchronize()
             dec_us.append(a.elapsed_time(b) * 1e3)
             call_us.append(a.elapsed_time(c) * 1e3)
-        del flush
+        del flush, clean
         pct = lambda v: {"p10": round(float(np.percentile(v, 10)), 2),
                          "median": round(float(np.median(v)), 2),
                          "p90": round(float(np.percentile(v, 90)), 2)}
         cold = {"reps": args.cold_reps, "decode_us": pct(dec_us), "call_us": pct(call_us),
                 "decode_kv_GB/s_median": round(wl.kv_bytes() / (np.median(dec_us) * 1e-6) / 1e9, 1),
-                "flush": "1 GiB read+write before each call"}
+                "flush": "1 GiB read+write, then a 512 MiB read, before each call"}
 
     ms_step = T / args.steps * 1e3
     t_app = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
@@ -239,8 +294,6 @@ def main():
     value = kv / (ms_step * 1e-3) / 1e9
     alg = decode_algorithmic_bytes(wl, psize if split else None)
     achieved = alg / (t_dec * 1e-6) / 1e9
-    khash = kernel_source_hash()
-    mode_key = f"{kernel}/{args.mode}{psize if split else ''}"
     traffic = load_traffic(khash, wl.name, mode_key)
 
     rec = {
@@ -261,7 +314,11 @@ def main():
         "pct_of_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": f"decode_{kernel}_kernel",
+                     "traffic": traffic,
+                     "traffic_over_algorithmic": round(traffic / alg, 4) if traffic else None,
+                     "kernel": f"decode_persistent_kernel<{'MfmaTile' if kernel == 'mfma' else 'ValuTile'}"
+                               f"<{kv_code}, {wl.head_dim}, {wl.block_size}, "
+                               f"{wl.num_q_heads // wl.num_kv_heads}>>",
                      "algorithmic_bytes_per_launch": alg, "avg_launch_us": round(t_dec, 2),
                      "kernel_hash": khash},
         "read_ceiling": ceiling,
