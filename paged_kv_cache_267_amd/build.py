@@ -22,6 +22,9 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
     # packed fp32 instructions stay off (see the device code notes)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # LDS is laid out by the kernels themselves: per-thread arrays stay in
+    # registers instead of being moved into spare LDS by the compiler
+    "-mllvm", "-disable-promote-alloca-to-lds",
 ]
 
 

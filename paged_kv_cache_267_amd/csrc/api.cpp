@@ -51,6 +51,8 @@ int check_decode(const void* query, const void* key_cache, const void* value_cac
   if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
     return PA_ERR_SHAPE;
   if ((long long)max_blocks_per_seq * block_size > (1ll << 30)) return PA_ERR_SHAPE;
+  // block-table entries are indexed with 32-bit integers on the device
+  if ((long long)num_seqs * max_blocks_per_seq >= (1ll << 31)) return PA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
   if (!group_supported(kv_dtype, num_q_heads / num_kv_heads)) return PA_ERR_UNSUPPORTED;

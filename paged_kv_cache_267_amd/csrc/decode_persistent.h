@@ -86,7 +86,7 @@ struct PdSmem {
   int32_t tbl[PD_TBL];               // staged block ids of the batch
   alignas(16) uint8_t q[SLOTS][G][T::QROWB];   // staged query rows of the batch
   SegMeta meta[SLOTS];
-  int32_t bcount, bnext_m, bnext_st, scan[2][PD_WAVES];
+  int32_t bcount, bnext_m, bnext_st, bused, scan[2][PD_WAVES];
   int32_t arrived[T::NPAR];          // deposits into each merge area (4 per use)
   int32_t done[T::NPAR];             // quarter merges out of each area (4 per use)
   typename T::WaveLds wl[PD_WAVES];  // per-wave scratch of the tile computation
@@ -269,7 +269,10 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
   int M = total / J;  // full rounds, then possibly one entry of the last round
   if (M * J < total && list_index(M) < total) ++M;
 
-  // k-th segment of the list -> (sequence, partition)
+  // k-th segment of the list -> (sequence, partition).  A workgroup asks for
+  // increasing k, so the search for a full partition's (or, unsorted, a
+  // partial segment's) sequence resumes where the previous one stopped.
+  int hint_f = 0, hint_p = 0;
   auto seg_of = [&](int k, int& si, int& pp) {
     const bool full = k < F;
     const int kk = full ? k : k - F;
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
       return;
     }
     const int32_t* pre = full ? sm.fpre : sm.ppre;
-    si = 0;
+    si = full ? hint_f : hint_p;
     for (;;) {
       const int i = si + lane;
       const int v = i < S ? pre[i + 1] : 0x7fffffff;
@@ -288,6 +291,8 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
       if (hit) { si += __builtin_ctzll(hit); break; }
       si += 64;
     }
+    if (full) hint_f = si;
+    else hint_p = si;
     const int L = uniform(sm.lens[si]);
     int nf, np, f0;
     counts(L, nf, np, f0);
@@ -392,6 +397,9 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
           b = (a / SPB + room) * SPB;
         }
         const int nblk = b > a ? (b + SPB - 1) / SPB - a / SPB : 0;
+        // table entries to stage: their index into block_tables for now
+        const int row0 = (s0 + si) * p.max_blocks + a / SPB;
+        for (int i = lane; i < nblk; i += 64) sm.tbl[used + i] = row0 + i;
         if (lane == 0) {
           SegMeta& md = sm.meta[cnt];
           md.s = si; md.p = pp; md.t0 = t0; md.t1 = t1;
@@ -409,6 +417,7 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
         sm.bcount = cnt;
         sm.bnext_m = next_m;
         sm.bnext_st = next_st;
+        sm.bused = used;
       }
     }
     __syncthreads();
@@ -417,20 +426,50 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
     bst = uniform(sm.bnext_st);
 
     // ---- stage block ids and queries of the batch ------------------------------------
-    for (int c = 0; c < nslot; ++c) {
-      const int si = uniform(sm.meta[c].s), a = uniform(sm.meta[c].st_a);
-      const int b = uniform(sm.meta[c].st_b), t = uniform(sm.meta[c].tbl);
-      const int blk0 = a / SPB, nblk = b > a ? (b + SPB - 1) / SPB - blk0 : 0;
-      const int32_t* trow = p.block_tables + (size_t)(s0 + si) * p.max_blocks + blk0;
-      for (int i = tid; i < nblk; i += NTH) {
-        const unsigned id = (unsigned)trow[i];
-        sm.tbl[t + i] = (int)(id > nb_max ? nb_max : id);
-      }
-      // G query rows of D * EQ bytes, 16 bytes per thread step
+    // Every load is issued before any is used, so staging costs one memory
+    // round trip: block ids (clamped into the pool) over their table indices,
+    // and the G query rows of D * EQ bytes of each slot, 16 bytes at a time.
+    {
       constexpr int QV = D * EQ / 16;
-      const uint8_t* qsrc = (const uint8_t*)p.q + ((size_t)(s0 + si) * Hq + hk * G) * D * EQ;
-      for (int i = tid; i < G * QV; i += NTH)
-        *(uint4*)&sm.q[c][i / QV][(i % QV) * 16] = *(const uint4*)(qsrc + (size_t)i * 16);
+      constexpr int TPT = PD_TBL / NTH;                              // table entries per thread
+      constexpr int QPT = (SLOTS * G * QV + NTH - 1) / NTH;          // query pieces per thread
+      static_assert(TPT == 8 && QPT <= 4, "staging registers");
+      const int ntbl = uniform(sm.bused), nq = nslot * G * QV;
+      // held in vector registers (not arrays, which the compiler would place
+      // in scratch memory)
+      i32x8_t tv = {0, 0, 0, 0, 0, 0, 0, 0};
+      u32x16_t qv = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int k = 0; k < TPT; ++k) {
+        const int t = tid + k * NTH;
+        if (t < ntbl) tv[k] = p.block_tables[(uint32_t)sm.tbl[t]];
+      }
+#pragma unroll
+      for (int k = 0; k < QPT; ++k) {
+        const int e = tid + k * NTH;
+        if (e < nq) {
+          const int c = e / (G * QV), r = e % (G * QV);
+          const uint8_t* qsrc =
+              (const uint8_t*)p.q + ((size_t)(s0 + sm.meta[c].s) * Hq + hk * G) * D * EQ;
+          const uint4 v = *(const uint4*)(qsrc + (size_t)r * 16);
+          qv[4 * k] = v.x; qv[4 * k + 1] = v.y; qv[4 * k + 2] = v.z; qv[4 * k + 3] = v.w;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < TPT; ++k) {
+        const int t = tid + k * NTH;
+        const unsigned id = (unsigned)tv[k];
+        if (t < ntbl) sm.tbl[t] = (int)(id > nb_max ? nb_max : id);
+      }
+#pragma unroll
+      for (int k = 0; k < QPT; ++k) {
+        const int e = tid + k * NTH;
+        if (e < nq) {
+          const int c = e / (G * QV), r = e % (G * QV);
+          *(uint4*)&sm.q[c][r / QV][(r % QV) * 16] =
+              make_uint4(qv[4 * k], qv[4 * k + 1], qv[4 * k + 2], qv[4 * k + 3]);
+        }
+      }
     }
     __syncthreads();
 
