@@ -41,7 +41,7 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_SRC) > os.path.getmtime(_LIB_PATH):
         build()
     lib = ctypes.CDLL(_LIB_PATH)
     P, I, F, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double
@@ -54,6 +54,7 @@ def _load():
     lib.ora_num_threads.argtypes = []
     lib.ora_num_threads.restype = I
     lib.ora_reshape_and_cache.argtypes = [P, P, P, P, P, I, I, I, I, I, I]
+    lib.ora_reshape_and_cache_fp8.argtypes = [P, P, I, P, P, P, I, I, I, I, I, F, F]
     lib.ora_reshape_and_cache.restype = I
     lib.ora_decode.argtypes = [P, P, P, P, P, I, F, I, I, I, I, I, I, I, I, F, F, P, I, P]
     lib.ora_decode.restype = None
@@ -110,6 +111,25 @@ def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, *, num_k
     rc = _load().ora_reshape_and_cache(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
                                        _ptr(slots), int(slots.shape[0]), num_kv_heads, head_dim,
                                        block_size, num_blocks, _DT[kv_dtype])
+    if rc != 0:
+        raise ValueError("slot outside the block pool")
+
+
+def reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, *, src_dtype,
+                          num_kv_heads, head_dim, block_size, num_blocks, k_scale,
+                          v_scale) -> None:
+    """In place: quantise each token's K/V (f32 or bf16 bits) to E4M3 codes
+    of x / scale and write them into its slot of the E4M3 caches."""
+    key = np.ascontiguousarray(key)
+    value = np.ascontiguousarray(value)
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int32)
+    assert key.dtype == _NP[src_dtype] and value.dtype == _NP[src_dtype]
+    assert key_cache.dtype == np.uint8 and value_cache.dtype == np.uint8
+    rc = _load().ora_reshape_and_cache_fp8(_ptr(key), _ptr(value), _DT[src_dtype],
+                                           _ptr(key_cache), _ptr(value_cache), _ptr(slots),
+                                           int(slots.shape[0]), num_kv_heads, head_dim,
+                                           block_size, num_blocks, float(k_scale),
+                                           float(v_scale))
     if rc != 0:
         raise ValueError("slot outside the block pool")
 

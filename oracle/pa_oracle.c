@@ -173,6 +173,41 @@ int ora_reshape_and_cache(const void* key, const void* value, void* key_cache, v
   return 0;
 }
 
+/*
+ * Quantise-on-write: each element of the new tokens' K (V) is divided by
+ * k_scale (v_scale) and stored as the nearest E4M3 code ([P3 s3.4]: a scale
+ * factor and zero point 0; [P1 s2.2]: an fp8_e4m3 cache).  Reading: the
+ * quotient is formed as one IEEE binary32 division of the binary32 source
+ * value (the precision the code is decided in), then encoded by
+ * ora_fp8_e4m3_encode (ties to even, saturating at 448, NaN -> 0x7F).
+ * Returns -1 if a non-negative slot lies outside the pool.
+ */
+int ora_reshape_and_cache_fp8(const void* key, const void* value, int src_dtype,
+                              uint8_t* key_cache, uint8_t* value_cache,
+                              const int32_t* slot_mapping, int num_tokens, int Hkv, int D, int bs,
+                              int num_blocks, float k_scale, float v_scale) {
+  int t, h, d;
+  for (t = 0; t < num_tokens; ++t) {
+    int slot = slot_mapping[t];
+    int b, o;
+    if (slot < 0) continue;
+    if ((int64_t)slot >= (int64_t)num_blocks * bs) return -1;
+    b = slot / bs;
+    o = slot % bs;
+    for (h = 0; h < Hkv; ++h)
+      for (d = 0; d < D; ++d) {
+        size_t src = ((size_t)t * Hkv + h) * D + d;
+        volatile float xk = (float)ora_widen(key, src, src_dtype);
+        volatile float xv = (float)ora_widen(value, src, src_dtype);
+        volatile float qk = xk / k_scale;   /* binary32 division */
+        volatile float qv = xv / v_scale;
+        key_cache[ora_k_index(ORA_FP8, Hkv, D, bs, b, h, d, o)] = ora_fp8_e4m3_encode((double)qk);
+        value_cache[ora_v_index(Hkv, D, bs, b, h, d, o)] = ora_fp8_e4m3_encode((double)qv);
+      }
+  }
+  return 0;
+}
+
 /* ---- decode -------------------------------------------------------------- */
 
 typedef struct {

@@ -377,3 +377,115 @@ def test_reshape_and_cache_rejects_slot_outside_pool():
         oracle.reshape_and_cache(key, key, kc, kc.copy(), np.array([32], np.int32),
                                  num_kv_heads=1, head_dim=64, block_size=16, num_blocks=2,
                                  kv_dtype="f32")
+
+
+# ---------------------------------------------------------------------------
+# quantise-on-write (E4M3 codes of x / scale)
+
+def _quant_case(src, D, bs, seed, scale_k, scale_v, extra=None):
+    rng = np.random.default_rng(seed)
+    H, NB, T = 2, 6, 9
+    xk = (rng.standard_normal((T, H, D)) * 40).astype(np.float32)
+    xv = (rng.standard_normal((T, H, D)) * 3).astype(np.float32)
+    if extra is not None:
+        n = min(extra.size, xk.size)
+        xk.reshape(-1)[:n] = extra[:n]
+        xv.reshape(-1)[:n] = extra[:n]
+    if src == "bf16":
+        k_in, v_in = W.to_bf16_bits(xk), W.to_bf16_bits(xv)
+        xk, xv = oracle.bf16_value(k_in).astype(np.float32), oracle.bf16_value(v_in).astype(np.float32)
+    else:
+        k_in, v_in = xk, xv
+    slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int32)
+    slots[2] = -1
+    kc = np.full(NB * H * D * bs, 0xAB, np.uint8)
+    vc = kc.copy()
+    oracle.reshape_and_cache_fp8(k_in, v_in, kc, vc, slots, src_dtype=src, num_kv_heads=H,
+                                 head_dim=D, block_size=bs, num_blocks=NB, k_scale=scale_k,
+                                 v_scale=scale_v)
+    return xk, xv, slots, kc.reshape(NB, H, D // 16, bs, 16), vc.reshape(NB, H, D, bs)
+
+
+def _torch_codes(x32, scale):
+    import torch
+    q = torch.from_numpy(x32) / torch.tensor(scale, dtype=torch.float32)   # binary32 quotient
+    return q.to(torch.float8_e4m3fn).view(torch.uint8).numpy(), q.numpy()
+
+
+@pytest.mark.parametrize("src", ["f32", "bf16"])
+@pytest.mark.parametrize("D,bs", [(64, 16), (128, 32)])
+def test_quantise_on_write_matches_torch_cast_and_layout(src, D, bs):
+    """Codes land where the cache layout puts element (b, h, d, o), and equal
+    torch's RNE float8_e4m3fn cast of the binary32 quotient wherever
+    |x / scale| <= 448 (the cast's saturation behaviour differs beyond)."""
+    sk, sv = 0.3713, 0.0127
+    xk, xv, slots, kv, vv = _quant_case(src, D, bs, 5 + D + bs, sk, sv)
+    H = xk.shape[1]
+    for t in range(xk.shape[0]):
+        if slots[t] < 0:
+            continue
+        b, o = divmod(int(slots[t]), bs)
+        got_k = kv[b, :, :, o, :].reshape(H, D)
+        got_v = vv[b, :, :, o]
+        for got, x, s in ((got_k, xk[t], sk), (got_v, xv[t], sv)):
+            want, q = _torch_codes(x, s)
+            inr = np.abs(q) <= 448
+            assert np.array_equal(got[inr], want[inr])
+            assert np.all(got[~inr] == np.where(q[~inr] > 0, 0x7E, 0xFE))
+    # untouched slots keep their bytes
+    written = {int(s) for s in slots if s >= 0}
+    for b in range(kv.shape[0]):
+        for o in range(bs):
+            if b * bs + o not in written:
+                assert np.all(kv[b, :, :, o, :] == 0xAB) and np.all(vv[b, :, :, o] == 0xAB)
+
+
+def test_quantise_on_write_specials():
+    """Scale 1: signed zeros, NaN (-> 0x7F), saturation of infinities and of
+    values at or past 448, and the ties of the RNE rule (E4M3 value
+    (1 + m/8) * 2^(e-7); subnormal quantum 2^-9)."""
+    x = np.array([0.0, -0.0, np.nan, -np.nan, np.inf, -np.inf, 448.0, 464.0, 1e30, -1e30,
+                  2.0 ** -10,                  # half a quantum: tie -> 0
+                  2.0 ** -10 * (1 + 2 ** -20),  # just above: 1
+                  3 * 2.0 ** -10,              # 1.5 quanta: tie -> 2 (even)
+                  432.0,                       # between 416 (0x7D) and 448: tie -> 0x7E
+                  -424.0,                      # below the tie: -416 = 0xFD
+                  2.0 ** -6],                  # smallest normal: 0x08
+                 np.float32)
+    want = [0x00, 0x80, 0x7F, 0x7F, 0x7E, 0xFE, 0x7E, 0x7E, 0x7E, 0xFE,
+            0x00, 0x01, 0x02, 0x7E, 0xFD, 0x08]
+    xk, xv, slots, kv, vv = _quant_case("f32", 64, 16, 3, 1.0, 1.0, extra=x)
+    b, o = divmod(int(slots[0]), 16)
+    assert list(kv[b, 0, :, o, :].reshape(64)[:x.size]) == want
+    assert list(vv[b, 0, :x.size, o]) == want
+
+
+def test_quantise_on_write_decides_on_the_binary32_quotient():
+    """A quotient that is inexact in binary32 but rounds exactly onto an E4M3
+    tie point: the binary32 path ties to even, an fp64 quotient would not."""
+    rng = np.random.default_rng(0)
+    found = None
+    for _ in range(200000):
+        s = np.float32(rng.uniform(0.3, 3.0))
+        mid = np.float32(1.0625)                    # between codes 1.0 and 1.125
+        x = np.float32(mid * s)
+        for cand in (x, np.nextafter(x, np.float32(np.inf)), np.nextafter(x, np.float32(0))):
+            q32 = np.float32(cand / s)
+            q64 = np.float64(cand) / np.float64(s)
+            if q32 == mid and q64 != np.float64(mid):
+                found = (cand, s, q64)
+                break
+        if found:
+            break
+    assert found, "no binary32 tie case found"
+    x, s, q64 = found
+    xk = np.zeros((1, 1, 64), np.float32)
+    xk[0, 0, 0] = x
+    kc = np.zeros(64 * 16, np.uint8)
+    vc = kc.copy()
+    oracle.reshape_and_cache_fp8(xk, xk, kc, vc, np.array([0], np.int32), src_dtype="f32",
+                                 num_kv_heads=1, head_dim=64, block_size=16, num_blocks=1,
+                                 k_scale=float(s), v_scale=float(s))
+    code = kc.reshape(1, 1, 4, 16, 16)[0, 0, 0, 0, 0]
+    assert code == 0x38                              # 1.0: the tie went to the even code
+    assert oracle.fp8_e4m3_encode(q64) == (0x39 if q64 > 1.0625 else 0x38)
