@@ -180,6 +180,10 @@ def main():
                     help="no GPU run: store the decode kernel's HBM bytes per launch from "
                          "rocprofv3 counter CSVs of this configuration (with "
                          "--calibrate-copy-mib set as in those runs)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the step as eager launches only (default: the step is also "
+                         "captured in a HIP graph, checked against the eager result, and the "
+                         "headline is the graph replay time)")
     ap.add_argument("--cold-reps", type=int, default=30,
                     help="calls timed one by one after a 1 GiB read+write flush of the caches "
                          "(0: skip)")
@@ -253,6 +257,38 @@ def main():
         e[3].record(stream)
     torch.cuda.synchronize()
     T = time.perf_counter() - t0
+    T_eager = T
+
+    graph = None
+    if not args.no_graph:
+        # the same step captured once and replayed: launch gaps leave the step
+        ref = dw.out.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            dw.step(split=split)
+        for _ in range(3):                  # every replay must reproduce the eager output
+            dw.out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(dw.out.view(torch.int16) if dw.out.dtype == torch.bfloat16
+                               else dw.out, ref.view(torch.int16) if ref.dtype == torch.bfloat16
+                               else ref):
+                raise RuntimeError("graph replay differs from the eager step")
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        gev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        t0 = time.perf_counter()
+        gev[0].record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        gev[1].record(stream)
+        torch.cuda.synchronize()
+        T = time.perf_counter() - t0
+        graph = {"ms_per_step": round(T / args.steps * 1e3, 4),
+                 "event_us_per_step": round(gev[0].elapsed_time(gev[1]) * 1e3 / args.steps, 2),
+                 "check": "3 replays bit-identical to the eager step output"}
+        del g
 
     cold = None
     if args.cold_reps > 0:
@@ -307,7 +343,10 @@ def main():
                    "partition_size": psize if split else None, "parallelism": "single GPU"},
         "step_breakdown_us": {"reshape_and_cache": round(t_app, 2), "decode": round(t_dec, 2),
                               "reduce_lse": round(t_red, 2),
+                              "eager_wall_per_step": round(T_eager / args.steps * 1e6, 2),
                               "wall_per_step": round(ms_step * 1e3, 2)},
+        "step_timing": "hip graph replay of the step" if graph else "eager launches",
+        "graph": graph,
         "kv_bytes_per_step": kv,
         "unique_kv_bytes_per_step": int(wl.unique_kv_bytes()),
         "cold": cold,

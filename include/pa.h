@@ -109,6 +109,23 @@ int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, vo
                          void* stream);
 
 /*
+ * pa_reshape_and_cache_fp8 -- the same write into E4M3 caches, quantising on
+ * the way ([P3 s3.4]: an FP8 KV cache with a per-tensor scale and zero point
+ * 0; [P1 s2.2]: fp8_e4m3).  key / value are [num_tokens][num_kv_heads]
+ * [head_dim] in src_dtype (PA_F32 or PA_BF16); element x of K is stored as the
+ * E4M3 code nearest to the binary32 quotient x / k_scale (ties to even,
+ * saturating at +-448 including infinities, NaN -> 0x7F), V likewise with
+ * v_scale.  Caches, slots, alignment and errors as pa_reshape_and_cache;
+ * k_scale and v_scale must be finite and > 0 (PA_ERR_SHAPE otherwise).  The
+ * decode entry points then read the cache with kv_dtype = PA_FP8_E4M3 and the
+ * same scales.
+ */
+int pa_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
+                             void* value_cache, const int32_t* slot_mapping, int num_tokens,
+                             int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                             int src_dtype, float k_scale, float v_scale, void* stream);
+
+/*
  * pa_decode -- one query per sequence against its paged K/V, in one pass per
  * (sequence, KV head) ([P3 s2.2/s2.3], [P1 s2.2/s2.3]).
  *   For query head h of sequence s, with L = seq_lens[s], G = Hq/Hkv,

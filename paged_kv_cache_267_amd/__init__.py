@@ -23,7 +23,7 @@ STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE",
 EXPORTS = ("pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_reduce_lse",
            "pa_decode_split_workspace_bytes", "pa_fp8_e4m3_dequantize", "pa_status_string",
            "pa_last_hip_error", "pa_set_decode_kernel", "pa_get_decode_kernel",
-           "pa_decode_kernel_name", "pa_probe_gather_read")
+           "pa_decode_kernel_name", "pa_probe_gather_read", "pa_reshape_and_cache_fp8")
 KERNEL_CHOICES = {"auto": 0, "valu": 1, "mfma": 2}
 
 
@@ -67,11 +67,12 @@ def lib() -> ctypes.CDLL:
     L.pa_last_hip_error.argtypes = []
     L.pa_last_hip_error.restype = ctypes.c_char_p
     L.pa_probe_gather_read.argtypes = [P, P, ctypes.c_longlong, I, P, I, P]
+    L.pa_reshape_and_cache_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, F, P]
     L.pa_set_decode_kernel.argtypes = [I]
     L.pa_get_decode_kernel.argtypes = []
     L.pa_decode_kernel_name.argtypes = [I, I, I]
     L.pa_decode_kernel_name.restype = ctypes.c_char_p
-    for name in ("pa_probe_gather_read", "pa_set_decode_kernel", "pa_get_decode_kernel", "pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_reduce_lse",
+    for name in ("pa_reshape_and_cache_fp8", "pa_probe_gather_read", "pa_set_decode_kernel", "pa_get_decode_kernel", "pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_reduce_lse",
                  "pa_fp8_e4m3_dequantize"):
         getattr(L, name).restype = I
     _lib = L
@@ -123,6 +124,18 @@ def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, *, bl
         _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping), T, Hkv,
         D, block_size, _num_blocks(key_cache, Hkv, D, block_size), _dtype_code(key_cache),
         _stream(stream)))
+
+
+def pa_reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, *, block_size,
+                             k_scale, v_scale, stream=None) -> None:
+    """Quantise key/value [T, Hkv, D] (float32 or bfloat16) to E4M3 codes of
+    x / scale and write them into their slots of the E4M3 caches (uint8)."""
+    T, Hkv, D = key.shape
+    assert value.shape == key.shape and value.dtype == key.dtype and slot_mapping.shape[0] == T
+    _check(lib().pa_reshape_and_cache_fp8(
+        _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping), T, Hkv,
+        D, block_size, _num_blocks(key_cache, Hkv, D, block_size), _dtype_code(key),
+        float(k_scale), float(v_scale), _stream(stream)))
 
 
 def pa_decode(query, key_cache, value_cache, block_tables, seq_lens, *, block_size, scale, out,

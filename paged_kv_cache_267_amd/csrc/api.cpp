@@ -106,6 +106,27 @@ int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, vo
                                                  (hipStream_t)stream));
 }
 
+int pa_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
+                             void* value_cache, const int32_t* slot_mapping, int num_tokens,
+                             int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                             int src_dtype, float k_scale, float v_scale, void* stream) {
+  if (!key_cache || !value_cache) return PA_ERR_NULL;
+  if (src_dtype != PA_F32 && src_dtype != PA_BF16) return PA_ERR_DTYPE;
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PA_ERR_SHAPE;
+  if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+  if (!aligned16(key_cache) || !aligned16(value_cache)) return PA_ERR_ALIGN;
+  if (num_tokens == 0) return PA_OK;  // key / value / slot_mapping may be NULL then
+  if (!key || !value || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned16(key) || !aligned16(value)) return PA_ERR_ALIGN;
+  return hip_status(pa::launch_reshape_and_cache_fp8(
+      key, value, key_cache, value_cache, slot_mapping, num_tokens, num_kv_heads, head_dim,
+      block_size, num_blocks, elem_bytes(src_dtype), k_scale, v_scale, (hipStream_t)stream));
+}
+
 int pa_decode(const void* query, const void* key_cache, const void* value_cache,
               const int32_t* block_tables, const int32_t* seq_lens, int block_size, float scale,
               void* out, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,

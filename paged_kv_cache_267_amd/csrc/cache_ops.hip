@@ -43,6 +43,76 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   }
 }
 
+// E4M3 code of a binary32 value: nearest code, ties to even, saturating at
+// +-448 (infinities included), NaN -> 0x7F.  Codes are (1 + m/8) * 2^(e-7) for
+// exponent field e >= 1 and m/8 * 2^-6 for e = 0.  Normal range: the fp32
+// exponent and top 3 mantissa bits, rounded half to even on the 20 dropped
+// bits (a carry moves into the exponent), rebiased from 127 to 7.
+// Subnormal range (|q| < 2^-6): |q| * 2^9 rounded to an integer 0..8 (8 is
+// the smallest normal, code 0x08).
+__device__ __forceinline__ uint32_t e4m3_from_f32(float q) {
+  const uint32_t u = __float_as_uint(q);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;            // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;    // |q| >= 448
+  if (a < 0x3c800000u)                          // |q| < 2^-6
+    return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+  return sign | (r - ((127u - 7u) << 3));
+}
+
+// reshape_and_cache with quantisation ("vLLM 0.5 deep dive: PagedAttention
+// architecture", chenxutan.com, s3.4: an FP8 cache with a scale factor and
+// zero point 0): element x of a new token's K (V) is stored as the E4M3 code
+// of the binary32 quotient x / k_scale (x / v_scale).  One thread per (token,
+// head, 16-element group): 16 codes make one 16-byte K store; the same 16
+// elements of V go to 16 rows of the V tile.
+template <int SE>
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    const uint8_t* __restrict__ key, const uint8_t* __restrict__ value,
+    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, const int32_t* __restrict__ slots,
+    int num_tokens, int Hkv, int D, int bs, long long num_slots, float k_scale, float v_scale) {
+  const int groups = D / 16;
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)num_tokens * Hkv * groups;
+  if (gid >= total) return;
+  const int grp = (int)(gid % groups);
+  const int h = (int)((gid / groups) % Hkv);
+  const int t = (int)(gid / ((long long)groups * Hkv));
+  const int slot = slots[t];
+  if (slot < 0 || (long long)slot >= num_slots) return;
+  const int b = slot / bs, o = slot % bs;
+  const size_t src = (((size_t)t * Hkv + h) * D + (size_t)grp * 16) * SE;
+  const size_t tile = ((size_t)b * Hkv + h) * (size_t)D * bs;
+  float xk[16], xv[16];
+#pragma unroll
+  for (int c = 0; c < 16 * SE / 16; ++c) {   // 16-byte pieces of the 16 source elements
+    const uint4 k4 = *(const uint4*)(key + src + 16 * c);
+    const uint4 v4 = *(const uint4*)(value + src + 16 * c);
+    const uint32_t kw[4] = {k4.x, k4.y, k4.z, k4.w}, vw[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (SE == 4) {
+        xk[4 * c + w] = __uint_as_float(kw[w]);
+        xv[4 * c + w] = __uint_as_float(vw[w]);
+      } else {
+        xk[8 * c + 2 * w] = bf16_lo(kw[w]);
+        xk[8 * c + 2 * w + 1] = bf16_hi(kw[w]);
+        xv[8 * c + 2 * w] = bf16_lo(vw[w]);
+        xv[8 * c + 2 * w + 1] = bf16_hi(vw[w]);
+      }
+    }
+  }
+  uint32_t kq[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 16; ++e) kq[e >> 2] |= e4m3_from_f32(xk[e] / k_scale) << (8 * (e & 3));
+  *(uint4*)(kc + tile + ((size_t)grp * bs + o) * 16) = make_uint4(kq[0], kq[1], kq[2], kq[3]);
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    vc[tile + ((size_t)grp * 16 + e) * bs + o] = (uint8_t)e4m3_from_f32(xv[e] / v_scale);
+}
+
 // Merge of per-partition results by their log-sum-exp: for each (sequence,
 // query head) with keys [lo, L), the partitions p with [pP, (p+1)P) meeting that
 // range are combined as sum_p e^(lse_p - M) o_p / sum_p e^(lse_p - M).
@@ -212,6 +282,25 @@ static void launch_reduce_d(const float* part_out, const float* part_lse,
   else
     launch_reduce_rows<OUT_BF16, D, 1>(part_out, part_lse, seq_lens, rows, Hq, P, max_parts,
                                        window, out, stream);
+}
+
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* kc, void* vc,
+                                        const int32_t* slots, int T, int Hkv, int D, int bs,
+                                        int num_blocks, int src_bytes, float k_scale,
+                                        float v_scale, hipStream_t stream) {
+  const long long total = (long long)T * Hkv * (D / 16);
+  if (total == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  const long long nslots = (long long)num_blocks * bs;
+  const uint8_t *k8 = (const uint8_t*)key, *v8 = (const uint8_t*)value;
+  uint8_t *kc8 = (uint8_t*)kc, *vc8 = (uint8_t*)vc;
+  if (src_bytes == 4)
+    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<4>, dim3(blocks), dim3(256), 0, stream, k8,
+                       v8, kc8, vc8, slots, T, Hkv, D, bs, nslots, k_scale, v_scale);
+  else
+    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<2>, dim3(blocks), dim3(256), 0, stream, k8,
+                       v8, kc8, vc8, slots, T, Hkv, D, bs, nslots, k_scale, v_scale);
+  return hipGetLastError();
 }
 
 hipError_t launch_reduce_lse(const float* part_out, const float* part_lse,

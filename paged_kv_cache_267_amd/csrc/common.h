@@ -42,6 +42,7 @@ struct DecodeParams {
   int partition_size;   // tokens per partition (split); 0 = whole sequence
   int max_parts;
   int seq_begin, seq_count;  // sequences of this launch (persistent schedule)
+  int pairs;            // the grid is two workgroups per CU, j and j + J/2 of a head together
 };
 
 // ---- scalar conversions ------------------------------------------------------

@@ -34,6 +34,10 @@ hipError_t dispatch_decode(const DecodeParams& p, int kv_dtype, int D, int BS, i
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc, void* vc,
                                     const int32_t* slots, int T, int Hkv, int D, int bs,
                                     int num_blocks, int elem_bytes, hipStream_t stream);
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* kc, void* vc,
+                                        const int32_t* slots, int T, int Hkv, int D, int bs,
+                                        int num_blocks, int src_bytes, float k_scale,
+                                        float v_scale, hipStream_t stream);
 hipError_t launch_reduce_lse(const float* part_out, const float* part_lse,
                              const int32_t* seq_lens, int S, int Hq, int D, int P, int max_parts,
                              int window, void* out, bool out_bf16, hipStream_t stream);

@@ -156,3 +156,21 @@ def test_probe_validation():
     assert L.pa_probe_gather_read(A, A, -1, 4096, A, 0, NULL) == 3
     assert L.pa_probe_gather_read(NULL, A, 4, 4096, A, 0, NULL) == 1
     assert L.pa_probe_gather_read(ODD, A, 4, 4096, A, 0, NULL) == 7
+
+
+def test_reshape_and_cache_fp8_validation():
+    L = pa.lib()
+    ok = [A, A, A, A, A, 4, 2, 128, 16, 8, 1, 0.5, 0.25, NULL]
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return L.pa_reshape_and_cache_fp8(*a)
+    assert call(2, NULL) == 1 and call(0, NULL) == 1 and call(4, NULL) == 1
+    assert call(10, 2) == 2           # E4M3 source: use the bit copy
+    assert call(10, 7) == 2
+    assert call(5, -1) == 3
+    assert call(11, 0.0) == 3 and call(12, -1.0) == 3 and call(11, float("inf")) == 3
+    assert call(12, float("nan")) == 3
+    assert call(7, 96) == 4 and call(8, 64) == 4
+    assert call(0, ODD) == 7 and call(2, ODD) == 7
+    assert call(5, 0) == 0            # zero tokens: no-op

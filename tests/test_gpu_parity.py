@@ -121,6 +121,53 @@ def test_reshape_and_cache_skips_negative_and_out_of_pool_slots():
     assert len(ok) == 3
 
 
+@pytest.mark.parametrize("src", ["bf16", "f32"])
+def test_reshape_and_cache_fp8_bit_exact(src):
+    """Quantise-on-write against the oracle, whole caches bit for bit: every
+    bf16 bit pattern (NaN, infinities, subnormals included) at three scales;
+    f32 values spread over the E4M3 range, ties and specials."""
+    import torch
+    import paged_kv_cache_267_amd as pa
+    H, D, bs, NB = 2, 128, 16, 24
+    rng = np.random.default_rng(61)
+    if src == "bf16":
+        bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+        rng.shuffle(bits)
+        k_in = bits.reshape(-1, H, D)
+        v_in = np.roll(bits, 1000).reshape(-1, H, D)
+        k_dev = torch.from_numpy(k_in.view(np.int16)).cuda().view(torch.bfloat16)
+        v_dev = torch.from_numpy(v_in.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        n = 96 * H * D
+        x = (rng.standard_normal(n) * np.exp(rng.uniform(-14, 7, n))).astype(np.float32)
+        ties = (np.arange(1, 15) * 2.0 ** -10).astype(np.float32)       # subnormal ties
+        mids = np.array([432.0, 440.0, 1.0625, 3.25, -6.5, 2.0 ** -7 * 1.0625], np.float32)
+        specials = np.array([0.0, -0.0, np.nan, np.inf, -np.inf, 448.0, 464.0, 1e38, 2.0 ** -149],
+                            np.float32)
+        x[:ties.size + mids.size + specials.size] = np.concatenate([ties, mids, specials])
+        k_in = x.reshape(-1, H, D)
+        v_in = -x[::-1].copy().reshape(-1, H, D)
+        k_dev = torch.from_numpy(k_in).cuda()
+        v_dev = torch.from_numpy(v_in).cuda()
+    T = k_in.shape[0]
+    for sk, sv in ((1.0, 1.0), (0.0371, 3.7), (1.0 / 448, 0.5)):
+        announce(f"quantise-on-write {src} scales {sk} {sv}")
+        slots = rng.choice(NB * bs * 2, size=T, replace=False).astype(np.int32)
+        slots[slots >= NB * bs] = -1                   # about half the tokens are skipped
+        kc_o = np.full(NB * H * D * bs, 0x5A, np.uint8)
+        vc_o = kc_o.copy()
+        oracle.reshape_and_cache_fp8(k_in, v_in, kc_o, vc_o, slots, src_dtype=src,
+                                     num_kv_heads=H, head_dim=D, block_size=bs, num_blocks=NB,
+                                     k_scale=sk, v_scale=sv)
+        kc = torch.full((NB * H * D * bs,), 0x5A, dtype=torch.uint8, device="cuda")
+        vc = kc.clone()
+        pa.pa_reshape_and_cache_fp8(k_dev, v_dev, kc, vc, torch.from_numpy(slots).cuda(),
+                                    block_size=bs, k_scale=sk, v_scale=sv)
+        torch.cuda.synchronize()
+        assert np.array_equal(kc.cpu().numpy(), kc_o), "K codes differ"
+        assert np.array_equal(vc.cpu().numpy(), vc_o), "V codes differ"
+
+
 # ---------------------------------------------------------------------------
 # decode parity on small cases spanning several tiles and ragged tails
 
@@ -336,3 +383,40 @@ def test_config5_window_poison_variant():
         with pa.decode_kernel(k):
             dw = gpu_run(wl, split=True)
         assert_close(dw.out_f64()[rows], ref, "fp8_e4m3", f"cfg5-skip kernel={k}")
+
+
+# ---------------------------------------------------------------------------
+# the step captured in a HIP graph
+
+@pytest.mark.parametrize("kvdt", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("split", [False, True])
+def test_graph_replay_matches_eager(kvdt, split):
+    """append + decode (+ merge) captured once: several replays, with eager work
+    and synchronisation between them, each equal bit for bit to the eager step
+    and close to the oracle."""
+    import torch
+    from paged_kv_cache_267_amd.harness import DeviceWorkload
+    wl = W.random_case(97, seq_lens=[0, 3, 150, 600, 1500, 77], num_q_heads=16, num_kv_heads=2,
+                       head_dim=128, block_size=16, kv_dtype=kvdt, sliding_window=500,
+                       partition_size=128)
+    kc, vc = oracle_caches(wl)
+    ref_o = oracle_decode(wl, kc, vc)
+    for k in kernels(kvdt):
+        announce(f"graph replay {kvdt} split={split} kernel={k}")
+        with pa.decode_kernel(k):
+            dw = DeviceWorkload(wl)
+            dw.fill_history()
+            dw.step(split=split)
+            torch.cuda.synchronize()
+            eager = dw.out.clone()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                dw.step(split=split)
+            for _ in range(3):
+                dw.out.zero_()
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                assert torch.equal(dw.out.view(torch.int16), eager.view(torch.int16))
+            del g
+        assert_close(dw.out_f64(), ref_o, kvdt, f"graph ({k})")
