@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace pa {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -15,6 +17,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x32_t __attribute__((ext_vector_type(32)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };

@@ -479,12 +479,12 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
       constexpr int QV = D * EQ / 16;
       constexpr int TPT = PD_TBL / NTH;                              // table entries per thread
       constexpr int QPT = (SLOTS * G * QV + NTH - 1) / NTH;          // query pieces per thread
-      static_assert(TPT == 8 && QPT <= 4, "staging registers");
+      static_assert(TPT == 8 && QPT <= 8, "staging registers");
       const int ntbl = uniform(sm.bused), nq = nslot * G * QV;
       // held in vector registers (not arrays, which the compiler would place
       // in scratch memory)
-      i32x8_t tv = {0, 0, 0, 0, 0, 0, 0, 0};
-      u32x16_t qv = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+      i32x8_t tv = {};
+      typename std::conditional<QPT <= 4, u32x16_t, u32x32_t>::type qv = {};
 #pragma unroll
       for (int k = 0; k < TPT; ++k) {
         const int t = tid + k * NTH;
