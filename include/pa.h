@@ -38,7 +38,8 @@
  *     (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).  bf16 and f32 outputs are
  *     rounded to nearest even from fp32.
  *   - GQA: G = num_q_heads / num_kv_heads; query head h reads KV head h / G.
- *     Supported: head_dim in {64, 128}, block_size in {16, 32},
+ *     Supported: head_dim in {64, 128}, block_size in {16, 32, 64} (the
+ *     sizes [P3 s3.1] offers),
  *     G in {1, 2, 4, 8} for every KV dtype and G = 16 for bf16 / FP8 KV.
  *
  * Layouts (element = one cache entry; X = 16 / element bytes, so one X-group
@@ -181,6 +182,19 @@ int pa_reduce_lse(const float* part_out, const float* part_lse, const int32_t* s
                   int num_seqs, int num_q_heads, int head_dim, int partition_size,
                   int max_num_partitions, int sliding_window, void* out, int out_dtype,
                   void* stream);
+
+/*
+ * pa_choose_block_size -- the automatic block size of [P3 s3.1] (16, 32 or 64
+ * tokens; short requests want small pages, long ones large pages) and of the
+ * tuning notes at the end of [P3] (small blocks: flexible, more to manage;
+ * large blocks: simple, may waste).  Reading: the largest of 64, 32 and 16
+ * whose tail waste over the given lengths, sum(ceil(L / bs) * bs - L), is at
+ * most max_waste_frac * sum(L); 16 if none is.  seq_lens is a HOST array of n
+ * expected lengths (negative values count as 0); an all-zero set gives 16.
+ * Returns the block size, or -PA_ERR_NULL (seq_lens NULL with n > 0),
+ * -PA_ERR_SHAPE (n < 0, or max_waste_frac not in (0, 1]).
+ */
+int pa_choose_block_size(const int32_t* seq_lens, int n, double max_waste_frac);
 
 /* Bytes of part_out + part_lse for pa_decode_split (part_lse starts at
    offset num_seqs*num_q_heads*max_num_partitions*head_dim*4). */

@@ -23,7 +23,8 @@ STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE",
 EXPORTS = ("pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_reduce_lse",
            "pa_decode_split_workspace_bytes", "pa_fp8_e4m3_dequantize", "pa_status_string",
            "pa_last_hip_error", "pa_set_decode_kernel", "pa_get_decode_kernel",
-           "pa_decode_kernel_name", "pa_probe_gather_read", "pa_reshape_and_cache_fp8")
+           "pa_decode_kernel_name", "pa_probe_gather_read", "pa_reshape_and_cache_fp8",
+           "pa_choose_block_size")
 KERNEL_CHOICES = {"auto": 0, "valu": 1, "mfma": 2}
 
 
@@ -68,11 +69,12 @@ def lib() -> ctypes.CDLL:
     L.pa_last_hip_error.restype = ctypes.c_char_p
     L.pa_probe_gather_read.argtypes = [P, P, ctypes.c_longlong, I, P, I, P]
     L.pa_reshape_and_cache_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, F, P]
+    L.pa_choose_block_size.argtypes = [P, I, ctypes.c_double]
     L.pa_set_decode_kernel.argtypes = [I]
     L.pa_get_decode_kernel.argtypes = []
     L.pa_decode_kernel_name.argtypes = [I, I, I]
     L.pa_decode_kernel_name.restype = ctypes.c_char_p
-    for name in ("pa_reshape_and_cache_fp8", "pa_probe_gather_read", "pa_set_decode_kernel", "pa_get_decode_kernel", "pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_reduce_lse",
+    for name in ("pa_choose_block_size", "pa_reshape_and_cache_fp8", "pa_probe_gather_read", "pa_set_decode_kernel", "pa_get_decode_kernel", "pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_reduce_lse",
                  "pa_fp8_e4m3_dequantize"):
         getattr(L, name).restype = I
     _lib = L
@@ -188,6 +190,17 @@ def pa_probe_gather_read(base, ids, chunk_bytes, sink, grid=0, stream=None) -> N
     """Bandwidth probe: read chunks base[ids[k] * chunk_bytes ...] (see pa.h)."""
     _check(lib().pa_probe_gather_read(_ptr(base), _ptr(ids), ids.numel(), int(chunk_bytes),
                                       _ptr(sink), int(grid), _stream(stream)))
+
+
+def pa_choose_block_size(seq_lens, max_waste_frac=0.05) -> int:
+    """Block size (16, 32 or 64) for a set of expected sequence lengths (host)."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    r = lib().pa_choose_block_size(ctypes.c_void_p(lens.ctypes.data) if lens.size else None,
+                                   int(lens.size), float(max_waste_frac))
+    if r < 0:
+        _check(-r)
+    return int(r)
 
 
 def pa_set_decode_kernel(choice) -> None:

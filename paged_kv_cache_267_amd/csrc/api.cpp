@@ -54,7 +54,7 @@ int check_decode(const void* query, const void* key_cache, const void* value_cac
   // block-table entries are indexed with 32-bit integers on the device
   if ((long long)num_seqs * max_blocks_per_seq >= (1ll << 31)) return PA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
-  if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+  if (block_size != 16 && block_size != 32 && block_size != 64) return PA_ERR_UNSUPPORTED;
   if (!group_supported(kv_dtype, num_q_heads / num_kv_heads)) return PA_ERR_UNSUPPORTED;
   if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache)) return PA_ERR_ALIGN;
   return PA_OK;
@@ -95,7 +95,7 @@ int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, vo
   if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
     return PA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
-  if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+  if (block_size != 16 && block_size != 32 && block_size != 64) return PA_ERR_UNSUPPORTED;
   if (!aligned16(key_cache) || !aligned16(value_cache)) return PA_ERR_ALIGN;
   if (num_tokens == 0) return PA_OK;  // key / value / slot_mapping may be NULL then
   if (!key || !value || !slot_mapping) return PA_ERR_NULL;
@@ -117,7 +117,7 @@ int pa_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache
   if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
     return PA_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
-  if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+  if (block_size != 16 && block_size != 32 && block_size != 64) return PA_ERR_UNSUPPORTED;
   if (!aligned16(key_cache) || !aligned16(value_cache)) return PA_ERR_ALIGN;
   if (num_tokens == 0) return PA_OK;  // key / value / slot_mapping may be NULL then
   if (!key || !value || !slot_mapping) return PA_ERR_NULL;
@@ -195,6 +195,22 @@ int pa_reduce_lse(const float* part_out, const float* part_lse, const int32_t* s
                                           head_dim, partition_size, max_num_partitions,
                                           sliding_window, out, out_dtype == PA_BF16,
                                           (hipStream_t)stream));
+}
+
+int pa_choose_block_size(const int32_t* seq_lens, int n, double max_waste_frac) {
+  if (n < 0 || !(max_waste_frac > 0.0 && max_waste_frac <= 1.0)) return -PA_ERR_SHAPE;
+  if (n > 0 && !seq_lens) return -PA_ERR_NULL;
+  long long tokens = 0, waste[3] = {0, 0, 0};
+  static const int sizes[3] = {64, 32, 16};
+  for (int i = 0; i < n; ++i) {
+    const long long L = seq_lens[i] > 0 ? seq_lens[i] : 0;
+    tokens += L;
+    for (int k = 0; k < 3; ++k) waste[k] += (L + sizes[k] - 1) / sizes[k] * sizes[k] - L;
+  }
+  if (tokens == 0) return 16;
+  for (int k = 0; k < 3; ++k)
+    if ((double)waste[k] <= max_waste_frac * (double)tokens) return sizes[k];
+  return 16;
 }
 
 size_t pa_decode_split_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,

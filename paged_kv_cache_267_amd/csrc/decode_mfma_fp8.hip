@@ -20,8 +20,10 @@ static hipError_t by_group(const DecodeParams& p, int G, hipStream_t s) {
 hipError_t decode_mfma_fp8(const DecodeParams& p, int D, int BS, int G, hipStream_t s) {
   if (D == 64 && BS == 16) return by_group<64, 16>(p, G, s);
   if (D == 64 && BS == 32) return by_group<64, 32>(p, G, s);
+  if (D == 64 && BS == 64) return by_group<64, 64>(p, G, s);
   if (D == 128 && BS == 16) return by_group<128, 16>(p, G, s);
   if (D == 128 && BS == 32) return by_group<128, 32>(p, G, s);
+  if (D == 128 && BS == 64) return by_group<128, 64>(p, G, s);
   return hipErrorInvalidValue;
 }
 

@@ -6,6 +6,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 import paged_kv_cache_267_amd as pa
@@ -57,7 +59,7 @@ def split(**kw):
     (dict(kvdt=9), 2),
     (dict(S=-1), 3), (dict(Hq=0), 3), (dict(Hq=6, Hkv=4), 3), (dict(mb=0), 3), (dict(nb=0), 3),
     (dict(win=-1), 3), (dict(scale=float("nan")), 3), (dict(S=70000), 3),
-    (dict(D=96), 4), (dict(bs=8), 4), (dict(bs=64), 4), (dict(Hq=6, Hkv=2), 4),
+    (dict(D=96), 4), (dict(bs=8), 4), (dict(bs=128), 4), (dict(Hq=6, Hkv=2), 4),
     (dict(Hq=64, Hkv=2), 4),
     (dict(out=ODD), 7), (dict(q=ODD), 7),
 ])
@@ -171,6 +173,31 @@ def test_reshape_and_cache_fp8_validation():
     assert call(5, -1) == 3
     assert call(11, 0.0) == 3 and call(12, -1.0) == 3 and call(11, float("inf")) == 3
     assert call(12, float("nan")) == 3
-    assert call(7, 96) == 4 and call(8, 64) == 4
+    assert call(7, 96) == 4 and call(8, 128) == 4
     assert call(0, ODD) == 7 and call(2, ODD) == 7
     assert call(5, 0) == 0            # zero tokens: no-op
+
+
+def test_choose_block_size():
+    choose = pa.pa_choose_block_size
+    assert choose([64, 128, 4096]) == 64                 # no tail waste at 64
+    assert choose([1, 2, 3]) == 16                       # short requests: small pages
+    assert choose([32, 96, 160]) == 32                   # no waste at 32; 32 per seq at 64
+    assert choose([]) == 16 and choose([0, -5]) == 16
+    # against the rule written out: the largest size whose waste <= frac * tokens
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        lens = rng.integers(-3, 5000, size=rng.integers(1, 40))
+        frac = float(rng.uniform(0.001, 0.3))
+        L = np.maximum(lens, 0)
+        want = 16
+        if L.sum() > 0:
+            for bs in (64, 32, 16):
+                if (-(-L // bs) * bs - L).sum() <= frac * L.sum():
+                    want = bs
+                    break
+        assert choose(lens, frac) == want
+    L = pa.lib()
+    assert L.pa_choose_block_size(None, 3, 0.05) == -1
+    assert L.pa_choose_block_size(None, -1, 0.05) == -3
+    assert L.pa_choose_block_size(None, 0, 0.0) == -3 and L.pa_choose_block_size(None, 0, 1.5) == -3

@@ -81,7 +81,8 @@ def test_fp8_device_conversion_all_codes():
 # reshape_and_cache: bit-exact against the oracle's cache
 
 @pytest.mark.parametrize("kvdt,D,bs", [("f32", 64, 16), ("bf16", 128, 16), ("bf16", 128, 32),
-                                       ("bf16", 64, 32), ("fp8_e4m3", 128, 16)])
+                                       ("bf16", 64, 32), ("fp8_e4m3", 128, 16),
+                                       ("bf16", 128, 64), ("fp8_e4m3", 64, 64)])
 def test_reshape_and_cache_bit_exact(kvdt, D, bs):
     announce(f"reshape_and_cache {kvdt} D{D} bs{bs}")
     qdt = "f32" if kvdt == "f32" else "bf16"
@@ -174,7 +175,7 @@ def test_reshape_and_cache_fp8_bit_exact(src):
 SMALL = []
 for kvdt in ("f32", "bf16", "fp8_e4m3"):
     for D in (64, 128):
-        for bs in (16, 32):
+        for bs in (16, 32, 64):
             for G in (1, 2, 4, 8, 16):
                 if G == 16 and kvdt == "f32":
                     continue  # not supported for f32 caches

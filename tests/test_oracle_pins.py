@@ -82,6 +82,8 @@ DENSE_CASES = [
     (4, 2, 128, 16, "bf16", "bf16", 37),
     (8, 2, 64, 16, "f32", "f32", 16),
     (4, 2, 128, 32, "bf16", "fp8_e4m3", 50),
+    (8, 2, 128, 64, "bf16", "bf16", 90),
+    (4, 4, 64, 64, "bf16", "fp8_e4m3", 0),
 ]
 
 
