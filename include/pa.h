@@ -88,7 +88,8 @@ typedef enum {
   PA_ERR_UNSUPPORTED = 4, /* head_dim / block_size / group size not built      */
   PA_ERR_PARTITION = 5,   /* bad partition_size / max_num_partitions           */
   PA_ERR_HIP = 6,         /* a kernel launch failed                            */
-  PA_ERR_ALIGN = 7        /* a buffer is not 16-byte aligned                   */
+  PA_ERR_ALIGN = 7,       /* a buffer is not 16-byte aligned                   */
+  PA_ERR_EXHAUSTED = 8    /* the block pool has too few free blocks            */
 } pa_status;
 
 /*
@@ -248,6 +249,49 @@ const char* pa_decode_kernel_name(int kv_dtype, int num_q_heads, int num_kv_head
  */
 int pa_probe_gather_read(const void* base, const int32_t* ids, long long num_chunks,
                          int chunk_bytes, unsigned* sink, int grid, void* stream);
+
+/*
+ * Host block manager (no device memory, no GPU calls): the pool of physical
+ * blocks behind the block tables.  [P3 s2.1]: a request holds ceil(n /
+ * block_size) blocks of a fixed pool, allocated as its tokens arrive; [P2
+ * "Core concept"] and [P1 s2.1]: block tables over non-contiguous blocks,
+ * requests with a common prefix share its blocks; [P1 s2.3]: blocks wholly
+ * before a sliding window are no longer needed.
+ *   - Blocks carry reference counts; the free list is FIFO.
+ *   - pa_bm_new_sequence(m, parent): parent < 0 starts an empty sequence;
+ *     otherwise the new sequence shares every block of parent (a fork).
+ *   - pa_bm_append(m, seq, n, slot_mapping, cow): appends n tokens, writing
+ *     the slot (block * block_size + offset) of each to slot_mapping[n], the
+ *     array pa_reshape_and_cache takes.  If the sequence's last block is
+ *     partly filled and shared, it is first replaced by a fresh block
+ *     (copy-on-write): cow[0] = old block, cow[1] = new block, and the caller
+ *     must copy block cow[0] to cow[1] in both caches before writing the new
+ *     tokens; else cow = {-1, -1}.  PA_ERR_EXHAUSTED (nothing changed) if the
+ *     pool lacks blocks.
+ *   - A block whose count drops to zero (pa_bm_free_sequence, or
+ *     pa_bm_release_before for blocks wholly before token first_token) is
+ *     parked with the caller's epoch (e.g. the step that last read it) and
+ *     returns to the free list only at pa_bm_reclaim(m, completed) with
+ *     epoch <= completed: a step still in flight never sees it reused.
+ *   - pa_bm_block_table writes a sequence's row (released blocks and padding
+ *     as -1) and returns its block count.
+ * Functions returning int give a count / id >= 0 or -pa_status, except
+ * pa_bm_append and pa_bm_free_sequence, which return a pa_status.  One host
+ * thread per manager.
+ */
+typedef struct pa_block_manager pa_block_manager;
+pa_block_manager* pa_bm_create(int num_blocks, int block_size);  /* NULL on bad sizes */
+void pa_bm_destroy(pa_block_manager* m);
+int pa_bm_num_free(const pa_block_manager* m);
+int pa_bm_new_sequence(pa_block_manager* m, int parent);
+int pa_bm_append(pa_block_manager* m, int seq, int num_tokens, int32_t* slot_mapping,
+                 int32_t* cow);
+int pa_bm_release_before(pa_block_manager* m, int seq, int first_token, uint64_t epoch);
+int pa_bm_free_sequence(pa_block_manager* m, int seq, uint64_t epoch);
+int pa_bm_reclaim(pa_block_manager* m, uint64_t completed_epoch);
+int pa_bm_block_table(const pa_block_manager* m, int seq, int32_t* row, int max_blocks);
+int pa_bm_seq_len(const pa_block_manager* m, int seq);
+int pa_bm_refcount(const pa_block_manager* m, int block);
 
 /* Human-readable name of a pa_status. */
 const char* pa_status_string(int status);

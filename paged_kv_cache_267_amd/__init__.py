@@ -17,14 +17,17 @@ LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpa.so")
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE",
-          4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_PARTITION", 6: "PA_ERR_HIP", 7: "PA_ERR_ALIGN"}
+          4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_PARTITION", 6: "PA_ERR_HIP", 7: "PA_ERR_ALIGN",
+          8: "PA_ERR_EXHAUSTED"}
 
 # exported symbols (include/pa.h)
 EXPORTS = ("pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_reduce_lse",
            "pa_decode_split_workspace_bytes", "pa_fp8_e4m3_dequantize", "pa_status_string",
            "pa_last_hip_error", "pa_set_decode_kernel", "pa_get_decode_kernel",
            "pa_decode_kernel_name", "pa_probe_gather_read", "pa_reshape_and_cache_fp8",
-           "pa_choose_block_size")
+           "pa_choose_block_size", "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free",
+           "pa_bm_new_sequence", "pa_bm_append", "pa_bm_release_before", "pa_bm_free_sequence",
+           "pa_bm_reclaim", "pa_bm_block_table", "pa_bm_seq_len", "pa_bm_refcount")
 KERNEL_CHOICES = {"auto": 0, "valu": 1, "mfma": 2}
 
 
@@ -70,6 +73,18 @@ def lib() -> ctypes.CDLL:
     L.pa_probe_gather_read.argtypes = [P, P, ctypes.c_longlong, I, P, I, P]
     L.pa_reshape_and_cache_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, F, P]
     L.pa_choose_block_size.argtypes = [P, I, ctypes.c_double]
+    U64 = ctypes.c_uint64
+    L.pa_bm_create.argtypes = [I, I]
+    L.pa_bm_create.restype = P
+    L.pa_bm_destroy.argtypes = [P]
+    L.pa_bm_destroy.restype = None
+    for name, args in (("pa_bm_num_free", [P]), ("pa_bm_new_sequence", [P, I]),
+                       ("pa_bm_append", [P, I, I, P, P]), ("pa_bm_release_before", [P, I, I, U64]),
+                       ("pa_bm_free_sequence", [P, I, U64]), ("pa_bm_reclaim", [P, U64]),
+                       ("pa_bm_block_table", [P, I, P, I]), ("pa_bm_seq_len", [P, I]),
+                       ("pa_bm_refcount", [P, I])):
+        getattr(L, name).argtypes = args
+        getattr(L, name).restype = I
     L.pa_set_decode_kernel.argtypes = [I]
     L.pa_get_decode_kernel.argtypes = []
     L.pa_decode_kernel_name.argtypes = [I, I, I]
@@ -201,6 +216,72 @@ def pa_choose_block_size(seq_lens, max_waste_frac=0.05) -> int:
     if r < 0:
         _check(-r)
     return int(r)
+
+
+class BlockManager:
+    """Host block pool manager (the pa_bm_* functions of include/pa.h)."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self._h = lib().pa_bm_create(int(num_blocks), int(block_size))
+        if not self._h:
+            raise PaError(3, "invalid pool size")
+        self.block_size = block_size
+
+    def close(self):
+        if self._h:
+            lib().pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover - interpreter shutdown
+            pass
+
+    @staticmethod
+    def _count(r: int) -> int:
+        if r < 0:
+            _check(-r)
+        return r
+
+    def num_free(self) -> int:
+        return self._count(lib().pa_bm_num_free(self._h))
+
+    def new_sequence(self, parent: int = -1) -> int:
+        return self._count(lib().pa_bm_new_sequence(self._h, int(parent)))
+
+    def append(self, seq: int, num_tokens: int):
+        """Slots of the new tokens (int32 array) and the copy-on-write pair."""
+        import numpy as np
+        slots = np.zeros(max(1, num_tokens), np.int32)
+        cow = np.zeros(2, np.int32)
+        _check(lib().pa_bm_append(self._h, int(seq), int(num_tokens),
+                                  ctypes.c_void_p(slots.ctypes.data),
+                                  ctypes.c_void_p(cow.ctypes.data)))
+        return slots[:num_tokens], (int(cow[0]), int(cow[1]))
+
+    def release_before(self, seq: int, first_token: int, epoch: int) -> int:
+        return self._count(lib().pa_bm_release_before(self._h, int(seq), int(first_token),
+                                                      int(epoch)))
+
+    def free_sequence(self, seq: int, epoch: int) -> None:
+        _check(lib().pa_bm_free_sequence(self._h, int(seq), int(epoch)))
+
+    def reclaim(self, completed_epoch: int) -> int:
+        return self._count(lib().pa_bm_reclaim(self._h, int(completed_epoch)))
+
+    def block_table(self, seq: int, max_blocks: int):
+        import numpy as np
+        row = np.zeros(max(1, max_blocks), np.int32)
+        self._count(lib().pa_bm_block_table(self._h, int(seq), ctypes.c_void_p(row.ctypes.data),
+                                            int(max_blocks)))
+        return row[:max_blocks]
+
+    def seq_len(self, seq: int) -> int:
+        return self._count(lib().pa_bm_seq_len(self._h, int(seq)))
+
+    def refcount(self, block: int) -> int:
+        return self._count(lib().pa_bm_refcount(self._h, int(block)))
 
 
 def pa_set_decode_kernel(choice) -> None:

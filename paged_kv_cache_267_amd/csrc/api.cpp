@@ -272,6 +272,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_PARTITION: return "invalid partition_size or max_num_partitions";
     case PA_ERR_HIP: return "HIP kernel launch failed";
     case PA_ERR_ALIGN: return "a buffer is not 16-byte aligned";
+    case PA_ERR_EXHAUSTED: return "the block pool has too few free blocks";
     default: return "unknown status";
   }
 }

@@ -122,7 +122,7 @@ def test_workspace_bytes():
 
 
 def test_status_strings():
-    for s in range(8):
+    for s in range(9):
         assert pa.lib().pa_status_string(s)
 
 
