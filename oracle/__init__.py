@@ -63,6 +63,8 @@ def _load():
     lib.ora_decode_split.restype = None
     lib.ora_reduce_lse.argtypes = [P, P, I, I, I, P]
     lib.ora_reduce_lse.restype = None
+    lib.ora_extend.argtypes = [P, P, P, P, P, P, I, F, I, I, I, I, I, I, I, I, F, F, P, I, P]
+    lib.ora_extend.restype = None
     _lib = lib
     return lib
 
@@ -181,6 +183,27 @@ def decode_split(query, key_cache, value_cache, block_tables, seq_lens, *, block
                              float(v_scale), int(partition_size), int(max_partitions),
                              _ptr(rows), int(rows.shape[0]), _ptr(po), _ptr(pl))
     return po, pl
+
+
+def extend(query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, *,
+           block_size, scale, num_kv_heads, q_dtype, kv_dtype, sliding_window=0, k_scale=1.0,
+           v_scale=1.0, rows=None) -> np.ndarray:
+    """Multi-token attention for rows (qrow * num_q_heads + h) of the query
+    array [num_tokens, num_q_heads, D]; sequence s owns query rows
+    query_start_loc[s] .. query_start_loc[s+1]-1.  float64 [nrows, D]."""
+    query, bt, sl = _common(query, q_dtype, key_cache, value_cache, kv_dtype, block_tables,
+                            seq_lens)
+    qsl = np.ascontiguousarray(query_start_loc, dtype=np.int32)
+    T, Hq, D = query.shape
+    S = sl.shape[0]
+    assert qsl.shape == (S + 1,) and qsl[0] == 0 and qsl[-1] == T and np.all(np.diff(qsl) >= 0)
+    rows = _rows(rows, T, Hq)
+    out = np.zeros((rows.shape[0], D), dtype=np.float64)
+    _load().ora_extend(_ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(bt), _ptr(sl),
+                       _ptr(qsl), block_size, float(scale), S, Hq, num_kv_heads, D, bt.shape[1],
+                       int(sliding_window), _DT[q_dtype], _DT[kv_dtype], float(k_scale),
+                       float(v_scale), _ptr(rows), int(rows.shape[0]), _ptr(out))
+    return out
 
 
 def reduce_lse(part_out, part_lse) -> np.ndarray:

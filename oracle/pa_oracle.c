@@ -23,6 +23,10 @@
  *         and section 2.3 (a 4K sliding window: K/V outside the window are
  *         masked, and blocks wholly outside it are not loaded).
  *   [P3 s3.4] FP8 KV cache with a scale factor and zero point 0.
+ *   [P3 s4.4, s5.2] prefix caching (requests reuse the cached KV of a shared
+ *         prompt and compute only what follows it) and chunked prefill (a
+ *         prompt enters in chunks): both attend a chunk of new query tokens
+ *         to the cached keys -- ora_extend.
  *
  * Every function below is the plain definition: each output row is computed
  * on its own, in fp64, with the full (not online) softmax and sums taken in
@@ -39,7 +43,12 @@
  *   - split partitions are aligned to logical token 0, the partition LSE is the
  *     natural-log log-sum-exp of the scaled scores, and an empty partition has
  *     LSE = -inf;
- *   - seq_len = 0 gives an all-zero output row.
+ *   - seq_len = 0 gives an all-zero output row;
+ *   - extend: a sequence's n new tokens are the last n of its L keys (their
+ *     K/V cached before the call), token i is at position L - n + i, and
+ *     attends causally: keys 0..p, and only the last W of them when W > 0
+ *     (the decode rule for the sequence cut after p); a token at a negative
+ *     position (n > L) gets a zero row.
  *
  * Cache layouts (the library boundary fixes them; see include/pa.h):
  *   value_cache [num_blocks][H_kv][D][bs]           (the order printed in [P3 s2.2])
@@ -220,12 +229,14 @@ typedef struct {
   double scale, k_scale, v_scale;
 } ora_problem;
 
-/* Softmax attention of query row (s, h) over logical keys [j0, j1):
+/* Softmax attention of query head h of query token row qrow (a row of the
+   query array; sequence s supplies the block table) over logical keys
+   [j0, j1):
    scores s_j = scale * sum_d q[d] * k_j[d]; m = max s_j; w_j = exp(s_j - m);
    Z = sum w_j; out[d] = sum_j w_j v_j[d] / Z.  Writes out[D] and returns
    m + ln Z (the natural-log LSE), or -inf for an empty range. */
-static double ora_attend(const ora_problem* P, int s, int h, int j0, int j1, double* out,
-                         double* scratch /* >= j1-j0 */) {
+static double ora_attend(const ora_problem* P, int s, int qrow, int h, int j0, int j1,
+                         double* out, double* scratch /* >= j1-j0 */) {
   int G = P->Hq / P->Hkv;
   int hk = h / G;
   int n = j1 - j0, j, d;
@@ -237,7 +248,7 @@ static double ora_attend(const ora_problem* P, int s, int h, int j0, int j1, dou
     int b = table[j / P->bs], o = j % P->bs;
     double dot = 0.0;
     for (d = 0; d < P->D; ++d) {
-      double qd = ora_widen(P->q, ((size_t)s * P->Hq + h) * P->D + d, P->q_dtype);
+      double qd = ora_widen(P->q, ((size_t)qrow * P->Hq + h) * P->D + d, P->q_dtype);
       double kd = ora_widen(P->kc, ora_k_index(P->kv_dtype, P->Hkv, P->D, P->bs, b, hk, d, o),
                             P->kv_dtype) * P->k_scale;
       dot += qd * kd;
@@ -281,7 +292,7 @@ void ora_decode(const void* q, const void* key_cache, const void* value_cache,
     int s = rows[r] / num_q_heads, h = rows[r] % num_q_heads;
     int L = seq_lens[s];
     double* scratch = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
-    ora_attend(&P, s, h, ora_window_lo(L, sliding_window), L > 0 ? L : 0,
+    ora_attend(&P, s, s, h, ora_window_lo(L, sliding_window), L > 0 ? L : 0,
                out + (size_t)r * head_dim, scratch);
     free(scratch);
   }
@@ -313,8 +324,43 @@ void ora_decode_split(const void* q, const void* key_cache, const void* value_ca
       if (a < lo) a = lo;
       if (b > L) b = L;
       part_lse[(size_t)r * max_parts + p] =
-          ora_attend(&P, s, h, a, b, part_out + ((size_t)r * max_parts + p) * head_dim, scratch);
+          ora_attend(&P, s, s, h, a, b, part_out + ((size_t)r * max_parts + p) * head_dim,
+                     scratch);
     }
+    free(scratch);
+  }
+}
+
+/* Extend (multi-token) attention.  Sequence s brings n_s = qsl[s+1] - qsl[s]
+   new query tokens (query rows qsl[s] .. qsl[s+1]-1), which are the last n_s
+   of its L = seq_lens[s] keys (their K/V already cached).  Its token i sits at
+   position p = L - n_s + i and attends causally to keys 0..p, within its own
+   window (keys p-W+1..p) when W > 0: the decode rule applied to the sequence
+   cut after position p.  query and out are [num_tokens][num_q_heads][D]; rows
+   lists qrow * num_q_heads + h.  A token at a negative position (n_s > L)
+   gets a zero row. */
+void ora_extend(const void* q, const void* key_cache, const void* value_cache,
+                const int32_t* block_tables, const int32_t* seq_lens,
+                const int32_t* query_start_loc, int block_size, float scale, int num_seqs,
+                int num_q_heads, int num_kv_heads, int head_dim, int max_blocks_per_seq,
+                int sliding_window, int q_dtype, int kv_dtype, float k_scale, float v_scale,
+                const int32_t* rows, int nrows, double* out) {
+  ora_problem P = {q, key_cache, value_cache, block_tables, seq_lens, block_size, num_seqs,
+                   num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sliding_window,
+                   q_dtype, kv_dtype, (double)scale, (double)k_scale, (double)v_scale};
+  int r;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (r = 0; r < nrows; ++r) {
+    int h = rows[r] % num_q_heads;
+    int qrow = rows[r] / num_q_heads;
+    int s = 0, Lp;
+    double* scratch;
+    while (s + 1 < num_seqs && query_start_loc[s + 1] <= qrow) ++s;
+    /* keys 0 .. position of this token */
+    Lp = seq_lens[s] - (query_start_loc[s + 1] - query_start_loc[s]) + (qrow - query_start_loc[s]) + 1;
+    scratch = (double*)malloc(sizeof(double) * (size_t)(Lp > 0 ? Lp : 1));
+    ora_attend(&P, s, qrow, h, ora_window_lo(Lp, sliding_window), Lp > 0 ? Lp : 0,
+               out + (size_t)r * head_dim, scratch);
     free(scratch);
   }
 }

@@ -53,7 +53,7 @@ class Workload:
     seq_lens: np.ndarray        # int32 [S]: keys each query sees (after the append)
     block_tables: np.ndarray    # int32 [S, max_blocks_per_seq], -1 padding
     num_blocks: int
-    query: np.ndarray           # [S, Hq, D]: float32, or uint16 bf16 bits
+    query: np.ndarray           # [S, Hq, D] (extend: [num_tokens, Hq, D]): float32 or bf16 bits
     hist_key: np.ndarray        # [T, Hkv, D] raw elements of tokens already in the cache
     hist_value: np.ndarray
     hist_slots: np.ndarray      # int32 [T]
@@ -66,6 +66,23 @@ class Workload:
     v_scale: float = 1.0
     partition_size: int = 512
     description: str = ""
+    # extend workloads: int32 [S + 1]; sequence s owns query rows
+    # query_start_loc[s] .. query_start_loc[s+1]-1 (None: decode, one row each)
+    query_start_loc: np.ndarray | None = None
+
+    @property
+    def q_lens(self) -> np.ndarray:
+        if self.query_start_loc is None:
+            return np.ones(self.num_seqs, dtype=np.int64)
+        return np.diff(self.query_start_loc.astype(np.int64))
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.query.shape[0])
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.q_lens.max()) if self.num_seqs else 0
 
     @property
     def max_blocks_per_seq(self) -> int:
@@ -86,9 +103,31 @@ class Workload:
             return np.minimum(L, self.sliding_window)
         return L
 
+    def key_span(self) -> np.ndarray:
+        """Keys the sequence's query tokens see together: from the first
+        token's window start to L (decode: effective_lens)."""
+        L = self.seq_lens.astype(np.int64)
+        if self.sliding_window <= 0:
+            return L
+        first = L - self.q_lens        # position of the first query token
+        return L - np.maximum(0, first + 1 - self.sliding_window)
+
+    def attended_pairs(self) -> int:
+        """(query token, key) pairs of one KV head's query group, summed over
+        sequences: sum over tokens of the keys each one attends to."""
+        total = 0
+        W = self.sliding_window
+        for L, n in zip(self.seq_lens.astype(np.int64), self.q_lens):
+            pos = np.arange(L - n, L, dtype=np.int64)
+            keys = pos + 1
+            if W > 0:
+                keys = np.minimum(keys, W)
+            total += int(np.maximum(keys, 0).sum())
+        return total
+
     def kv_bytes(self) -> int:
-        """K + V bytes one decode call must read: in-window tokens only."""
-        return int(self.effective_lens().sum()) * self.num_kv_heads * self.head_dim * 2 * \
+        """K + V bytes one call must read: in-window tokens only."""
+        return int(self.key_span().sum()) * self.num_kv_heads * self.head_dim * 2 * \
             ELEM_BYTES[self.kv_dtype]
 
     def unique_kv_bytes(self) -> int:
@@ -97,7 +136,7 @@ class Workload:
         total = 0
         for s in range(self.num_seqs):
             L = int(self.seq_lens[s])
-            lo = max(0, L - self.sliding_window) if self.sliding_window > 0 else 0
+            lo = L - int(self.key_span()[s])
             for j in range(lo, L):
                 key = (int(self.block_tables[s, j // self.block_size]), j % self.block_size)
                 if key not in seen:
@@ -140,16 +179,23 @@ def build(name: str, rng: np.random.Generator, seq_lens, *, num_q_heads: int,
           sliding_window: int = 0, shared_prefix: int = 0, pool_factor: float = 1.25,
           num_blocks: int | None = None, partition_size: int = 512,
           poison_out_of_window: bool = False, zero_query: bool = False,
-          description: str = "") -> Workload:
+          description: str = "", q_lens=None) -> Workload:
     """Draw one workload.  Draw order: (1) lengths are given, (2) the pool
     permutation, (3) Q, (4) K of every distinct token, (5) V likewise.
 
     Distinct tokens are ordered: the shared prefix (if any), then for each
-    sequence its private tokens in position order.  The last token of every
-    sequence (position L-1) is the step's new token: it is not in the history
-    and is written by the decode step's own cache append.
+    sequence its private tokens in position order.  The last q_lens[s] tokens
+    of sequence s (decode: q_lens = None, the last token, position L-1) are
+    the step's new tokens, one query row each: they are not in the history
+    and are written by the step's own cache append.
     """
     L = np.asarray(seq_lens, dtype=np.int64)
+    extend = q_lens is not None
+    n_new = np.asarray(q_lens, dtype=np.int64) if extend else np.ones_like(L)
+    assert n_new.shape == L.shape and (n_new >= 1).all() and (n_new <= L).all(), \
+        "every sequence brings 1..L new tokens"
+    if shared_prefix:
+        assert (L - n_new >= shared_prefix).all(), "new tokens lie after the shared prefix"
     S = int(L.shape[0])
     bs = int(block_size)
     D = int(head_dim)
@@ -190,9 +236,9 @@ def build(name: str, rng: np.random.Generator, seq_lens, *, num_q_heads: int,
     tok_pos = np.concatenate(tok_pos) if tok_pos else np.zeros(0, np.int64)
     T = int(tok_seq.shape[0])
     slots = (tables[tok_seq, tok_pos // bs].astype(np.int64) * bs + tok_pos % bs).astype(np.int32)
-    is_new = tok_pos == (L[tok_seq] - 1)
+    is_new = tok_pos >= (L[tok_seq] - n_new[tok_seq])
 
-    q = rng.standard_normal((S, num_q_heads, D), dtype=np.float32)
+    q = rng.standard_normal((int(n_new.sum()), num_q_heads, D), dtype=np.float32)
     if zero_query:
         q[:] = 0.0
     kf = rng.standard_normal((T, Hkv, D), dtype=np.float32)
@@ -209,8 +255,9 @@ def build(name: str, rng: np.random.Generator, seq_lens, *, num_q_heads: int,
 
     if poison_out_of_window and sliding_window > 0:
         for s in range(S):
-            lo = max(0, int(L[s]) - sliding_window)
-            tables[s, :lo // bs] = spare_block        # blocks wholly before the window
+            # blocks wholly before the window of the first query token
+            lo = max(0, int(L[s] - n_new[s]) + 1 - sliding_window)
+            tables[s, :lo // bs] = spare_block
 
     return Workload(
         name=name, num_seqs=S, num_q_heads=num_q_heads, num_kv_heads=Hkv, head_dim=D,
@@ -223,7 +270,9 @@ def build(name: str, rng: np.random.Generator, seq_lens, *, num_q_heads: int,
         new_slots=np.ascontiguousarray(slots[is_new]),
         scale=float(np.float32(1.0 / math.sqrt(D))), sliding_window=int(sliding_window),
         k_scale=k_scale, v_scale=v_scale, partition_size=int(partition_size),
-        description=description)
+        description=description,
+        query_start_loc=(np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
+                         if extend else None))
 
 
 # ---------------------------------------------------------------------------
@@ -283,11 +332,56 @@ def config(cfg: int, **overrides) -> Workload:
 def random_case(seed: int, *, seq_lens, num_q_heads=4, num_kv_heads=1, head_dim=128,
                 block_size=16, q_dtype="bf16", kv_dtype="bf16", sliding_window=0,
                 partition_size=64, shared_prefix=0, poison_out_of_window=False,
-                zero_query=False) -> Workload:
+                zero_query=False, q_lens=None) -> Workload:
     """A small case for parity sweeps (lengths given, everything else drawn)."""
     rng = np.random.default_rng(seed)
     return build(f"random_{seed}", rng, seq_lens, num_q_heads=num_q_heads,
                  num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=block_size,
                  q_dtype=q_dtype, kv_dtype=kv_dtype, sliding_window=sliding_window,
                  partition_size=partition_size, shared_prefix=shared_prefix,
-                 poison_out_of_window=poison_out_of_window, zero_query=zero_query)
+                 poison_out_of_window=poison_out_of_window, zero_query=zero_query,
+                 q_lens=q_lens)
+
+
+# ---------------------------------------------------------------------------
+# multi-token (extend) workloads: each sequence appends a chunk of new tokens
+# after its cached ones and attends causally over both.  Prefix caching
+# ("vLLM 0.5 deep dive: PagedAttention architecture", chenxutan.com, s4.4:
+# requests share a cached system prompt and compute only what follows it)
+# and chunked prefill (same page, s5.2: long prompts enter in chunks, with a
+# budget of 8192 batched tokens per step) both run this operation.
+
+EXTEND_SEED_BASE = 26800
+
+EXTEND_NAMES = ("chunked_prefill_bf16", "prefix_extend_bf16", "extend_fp8_window")
+
+
+def extend_config(name: str, **overrides) -> Workload:
+    """The named extend workloads, drawn from seed 26800 + their index."""
+    rng = np.random.default_rng(EXTEND_SEED_BASE + EXTEND_NAMES.index(name))
+    if name == "chunked_prefill_bf16":
+        prior = rng.integers(0, 3072, size=8, endpoint=True)
+        chunk = np.full(8, 1024)
+        return build(name, rng, prior + chunk, q_lens=chunk, num_q_heads=32, num_kv_heads=8,
+                     head_dim=128, block_size=16, q_dtype="bf16", kv_dtype="bf16",
+                     description="8 seqs x 1024-token chunks (8192 batched tokens) after "
+                                 "U[0,3072] cached tokens, 32/8 heads, D 128, bs 16, bf16",
+                     **overrides)
+    if name == "prefix_extend_bf16":
+        new = rng.integers(32, 256, size=32, endpoint=True)
+        return build(name, rng, 2048 + new, q_lens=new, num_q_heads=32, num_kv_heads=8,
+                     head_dim=128, block_size=16, q_dtype="bf16", kv_dtype="bf16",
+                     shared_prefix=2048,
+                     description="32 requests sharing a cached 2048-token prompt, each adding "
+                                 "U[32,256] new tokens, 32/8 heads, D 128, bs 16, bf16",
+                     **overrides)
+    if name == "extend_fp8_window":
+        prior = rng.integers(1024, 8192, size=16, endpoint=True)
+        chunk = np.full(16, 256)
+        return build(name, rng, prior + chunk, q_lens=chunk, num_q_heads=32, num_kv_heads=8,
+                     head_dim=128, block_size=16, q_dtype="bf16", kv_dtype="fp8_e4m3",
+                     sliding_window=4096,
+                     description="16 seqs x 256-token chunks after U[1024,8192] cached tokens, "
+                                 "32/8 heads, D 128, bs 16, fp8 e4m3 KV, window 4096",
+                     **overrides)
+    raise ValueError(f"no extend workload {name}")
