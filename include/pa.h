@@ -172,6 +172,43 @@ int pa_decode_split(const void* query, const void* key_cache, const void* value_
                     int max_num_partitions, float* part_out, float* part_lse, void* stream);
 
 /*
+ * pa_extend -- multi-token paged attention: each sequence appends a chunk of
+ * new query tokens after its cached ones and attends causally over the paged
+ * cache.  This is the attention step of prefix caching ([P3 s4.4]: requests
+ * that share a cached system prompt compute only the tokens after it) and of
+ * chunked prefill ([P3 s5.2]: a prompt enters in chunks).
+ *   Sequence s owns query rows query_start_loc[s] .. query_start_loc[s+1]-1
+ *   (n_s tokens); they are the last n_s of its L = seq_lens[s] keys, whose
+ *   K/V must already be in the cache (pa_reshape_and_cache).  Token i sits at
+ *   position p = L - n_s + i and, for query head h (KV head h / G):
+ *     lo = sliding_window > 0 ? max(0, p + 1 - sliding_window) : 0
+ *     s_j = scale * k_scale * sum_d q[d] k_j[d]            for j in [lo, p]
+ *     out = v_scale * sum_j softmax(s)_j v_j               (fp32 accumulation)
+ *   i.e. pa_decode's rule for the sequence cut after p.  A token at a
+ *   negative position (n_s > L) gets a zero row.  n_s = 1 for every sequence
+ *   is decode.
+ * query, out        [num_tokens][num_q_heads][head_dim] bf16 (q_dtype must be
+ *                   PA_BF16, out is bf16); kv_dtype PA_BF16 or PA_FP8_E4M3
+ *                   (PA_ERR_DTYPE otherwise).
+ * query_start_loc   int32 DEVICE array [num_seqs + 1], non-decreasing, from 0
+ *                   to num_tokens.
+ * max_query_len     >= every n_s (the launch is sized by it); 1 .. 2^20 when
+ *                   num_tokens > 0.
+ * Caches, block tables, seq_lens, head_dim, block_size, group sizes, scales,
+ * alignment and the clamping of out-of-range device data are as for
+ * pa_decode; rows of a sequence whose n_s exceeds max_query_len, or beyond
+ * num_tokens, are left unspecified.  num_seqs = 0 or num_tokens = 0 is a
+ * no-op once the dtypes pass (every pointer may then be NULL).  out must not
+ * alias any input.
+ */
+int pa_extend(const void* query, const void* key_cache, const void* value_cache,
+              const int32_t* block_tables, const int32_t* seq_lens,
+              const int32_t* query_start_loc, int block_size, float scale, void* out,
+              int num_seqs, int num_tokens, int max_query_len, int num_q_heads, int num_kv_heads,
+              int head_dim, int max_blocks_per_seq, int num_blocks, int sliding_window,
+              int q_dtype, int kv_dtype, float k_scale, float v_scale, void* stream);
+
+/*
  * pa_reduce_lse -- merge the partitions written by pa_decode_split:
  *   M = max_p lse_p;  out = sum_p e^(lse_p - M) o_p / sum_p e^(lse_p - M)
  * over the non-empty partitions of each row (found from seq_lens,

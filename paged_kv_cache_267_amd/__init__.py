@@ -27,7 +27,8 @@ EXPORTS = ("pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_reduce_ls
            "pa_decode_kernel_name", "pa_probe_gather_read", "pa_reshape_and_cache_fp8",
            "pa_choose_block_size", "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free",
            "pa_bm_new_sequence", "pa_bm_append", "pa_bm_release_before", "pa_bm_free_sequence",
-           "pa_bm_reclaim", "pa_bm_block_table", "pa_bm_seq_len", "pa_bm_refcount")
+           "pa_bm_reclaim", "pa_bm_block_table", "pa_bm_seq_len", "pa_bm_refcount",
+           "pa_extend")
 KERNEL_CHOICES = {"auto": 0, "valu": 1, "mfma": 2}
 
 
@@ -63,6 +64,7 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_split.argtypes = [P, P, P, P, P, I, F, I, I, I, I, I, I, I, I, I, F, F, I, I, P,
                                   P, P]
     L.pa_reduce_lse.argtypes = [P, P, P, I, I, I, I, I, I, P, I, P]
+    L.pa_extend.argtypes = [P, P, P, P, P, P, I, F, P, I, I, I, I, I, I, I, I, I, I, I, F, F, P]
     L.pa_decode_split_workspace_bytes.argtypes = [I, I, I, I]
     L.pa_decode_split_workspace_bytes.restype = ctypes.c_size_t
     L.pa_fp8_e4m3_dequantize.argtypes = [P, F, P, ctypes.c_longlong, P]
@@ -90,7 +92,7 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_kernel_name.argtypes = [I, I, I]
     L.pa_decode_kernel_name.restype = ctypes.c_char_p
     for name in ("pa_choose_block_size", "pa_reshape_and_cache_fp8", "pa_probe_gather_read", "pa_set_decode_kernel", "pa_get_decode_kernel", "pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_reduce_lse",
-                 "pa_fp8_e4m3_dequantize"):
+                 "pa_fp8_e4m3_dequantize", "pa_extend"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -178,6 +180,24 @@ def pa_decode_split(query, key_cache, value_cache, block_tables, seq_lens, *, bl
         _num_blocks(key_cache, num_kv_heads, D, block_size), int(sliding_window),
         _dtype_code(query), _dtype_code(key_cache), float(k_scale), float(v_scale),
         int(partition_size), int(max_num_partitions), _ptr(part_out), _ptr(part_lse),
+        _stream(stream)))
+
+
+def pa_extend(query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, *,
+              block_size, scale, out, num_kv_heads, max_query_len, sliding_window=0,
+              k_scale=1.0, v_scale=1.0, stream=None) -> None:
+    """Multi-token attention into ``out`` [num_tokens, Hq, D] (bf16): sequence s
+    owns query rows query_start_loc[s] .. query_start_loc[s+1]-1, the last of
+    its seq_lens[s] keys, each attending causally."""
+    T, Hq, D = query.shape
+    S = seq_lens.shape[0]
+    assert query_start_loc.shape[0] == S + 1
+    _check(lib().pa_extend(
+        _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables), _ptr(seq_lens),
+        _ptr(query_start_loc), block_size, float(scale), _ptr(out), S, T, int(max_query_len),
+        Hq, num_kv_heads, D, block_tables.shape[1],
+        _num_blocks(key_cache, num_kv_heads, D, block_size), int(sliding_window),
+        _dtype_code(query), _dtype_code(key_cache), float(k_scale), float(v_scale),
         _stream(stream)))
 
 

@@ -178,6 +178,53 @@ int pa_decode_split(const void* query, const void* key_cache, const void* value_
                                         num_q_heads / num_kv_heads, (hipStream_t)stream));
 }
 
+int pa_extend(const void* query, const void* key_cache, const void* value_cache,
+              const int32_t* block_tables, const int32_t* seq_lens,
+              const int32_t* query_start_loc, int block_size, float scale, void* out,
+              int num_seqs, int num_tokens, int max_query_len, int num_q_heads, int num_kv_heads,
+              int head_dim, int max_blocks_per_seq, int num_blocks, int sliding_window,
+              int q_dtype, int kv_dtype, float k_scale, float v_scale, void* stream) {
+  if (q_dtype != PA_BF16 || (kv_dtype != PA_BF16 && kv_dtype != PA_FP8_E4M3))
+    return PA_ERR_DTYPE;
+  if (num_seqs < 0 || num_tokens < 0) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;  // nothing to read or write
+  int st = check_decode(query, key_cache, value_cache, block_tables, seq_lens, block_size, scale,
+                        num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                        num_blocks, sliding_window, q_dtype, kv_dtype, k_scale, v_scale);
+  if (st != PA_OK) return st;
+  if (!query_start_loc || !out) return PA_ERR_NULL;
+  if (num_tokens < 0 || max_query_len < 0 || max_query_len > (1 << 20)) return PA_ERR_SHAPE;
+  if (num_tokens > 0 && max_query_len == 0) return PA_ERR_SHAPE;
+  if ((long long)num_tokens * num_q_heads * head_dim >= (1ll << 40)) return PA_ERR_SHAPE;
+  if (!aligned16(out)) return PA_ERR_ALIGN;
+  const int G = num_q_heads / num_kv_heads;
+  const long long pairs = (long long)num_seqs * num_kv_heads;
+  const long long cblocks = (((long long)max_query_len * G) + 127) / 128;  // >= the launch's
+  if (8 * ((pairs + 7) / 8) * cblocks >= (1ll << 31)) return PA_ERR_SHAPE;
+  pa::ExtendParams p{};
+  p.q = (const uint16_t*)query;
+  p.kc = (const char*)key_cache;
+  p.vc = (const char*)value_cache;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.qsl = query_start_loc;
+  p.out = (uint16_t*)out;
+  p.qk_scale = (float)((double)scale * (double)k_scale * 1.4426950408889634);
+  p.v_scale = v_scale;
+  p.num_seqs = num_seqs;
+  p.num_tokens = num_tokens;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  int lg = 0;
+  while ((1 << lg) < G) ++lg;
+  p.log2g = lg;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.window = sliding_window;
+  return hip_status(pa::launch_extend(p, kv_dtype == PA_BF16 ? pa::KV_BF16 : pa::KV_FP8, head_dim,
+                                      block_size, max_query_len, (hipStream_t)stream));
+}
+
 int pa_reduce_lse(const float* part_out, const float* part_lse, const int32_t* seq_lens,
                   int num_seqs, int num_q_heads, int head_dim, int partition_size,
                   int max_num_partitions, int sliding_window, void* out, int out_dtype,

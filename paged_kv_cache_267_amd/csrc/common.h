@@ -48,6 +48,24 @@ struct DecodeParams {
   int pairs;            // the grid is two workgroups per CU, j and j + J/2 of a head together
 };
 
+// Parameters of one multi-token (extend) launch.  Sequence s owns query rows
+// qsl[s] .. qsl[s+1]-1, the last of its seq_lens[s] keys.
+struct ExtendParams {
+  const uint16_t* q;    // [num_tokens][Hq][D] bf16
+  const char* kc;
+  const char* vc;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* qsl;   // [num_seqs + 1]
+  uint16_t* out;        // [num_tokens][Hq][D] bf16
+  float qk_scale;       // scale * k_scale * log2(e)
+  float v_scale;
+  int num_seqs, num_tokens, num_q_heads, num_kv_heads, log2g;
+  int max_blocks, num_blocks, window;
+  int cblocks;          // column blocks per (sequence, KV head)
+  int pairs;            // num_seqs * num_kv_heads
+};
+
 // ---- scalar conversions ------------------------------------------------------
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -31,6 +31,12 @@ bool decode_uses_mfma(int kv_dtype, int G);
 hipError_t dispatch_decode(const DecodeParams& p, int kv_dtype, int D, int BS, int G,
                            hipStream_t stream);
 
+// Multi-token attention (extend_mfma.hip): bf16 queries, bf16 or E4M3 caches,
+// head_dim {64, 128}, block_size {16, 32, 64}, any power-of-two group.
+// max_query_len bounds the chunk lengths; cblocks and pairs are filled in.
+hipError_t launch_extend(ExtendParams p, int kv_dtype, int D, int BS, int max_query_len,
+                         hipStream_t stream);
+
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc, void* vc,
                                     const int32_t* slots, int T, int Hkv, int D, int bs,
                                     int num_blocks, int elem_bytes, hipStream_t stream);

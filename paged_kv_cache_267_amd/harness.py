@@ -7,7 +7,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (pa_decode, pa_decode_split, pa_reduce_lse, pa_reshape_and_cache)
+from . import (pa_decode, pa_decode_split, pa_extend, pa_reduce_lse, pa_reshape_and_cache)
 from .workloads import POISON_BYTE, Workload
 
 
@@ -58,6 +58,8 @@ class DeviceWorkload:
         S, Hq, D = wl.num_seqs, wl.num_q_heads, wl.head_dim
         self.part_out = torch.empty((S, Hq, self.max_parts, D), dtype=torch.float32, device=d)
         self.part_lse = torch.empty((S, Hq, self.max_parts), dtype=torch.float32, device=d)
+        self.query_start_loc = (torch.from_numpy(wl.query_start_loc).to(d)
+                                if wl.query_start_loc is not None else None)
 
     # -- steps ------------------------------------------------------------------
     def fill_history(self):
@@ -90,6 +92,18 @@ class DeviceWorkload:
                       partition_size=self.partition_size,
                       sliding_window=self.wl.sliding_window, out=self.out, stream=stream)
         return self.out
+
+    def extend(self, stream=None):
+        """Multi-token attention of every sequence's new chunk (extend workloads)."""
+        pa_extend(self.query, self.key_cache, self.value_cache, self.block_tables,
+                  self.seq_lens, self.query_start_loc, out=self.out,
+                  max_query_len=self.wl.max_query_len, stream=stream, **self._kw())
+        return self.out
+
+    def step_extend(self, stream=None):
+        """One extend step: append the chunks' K/V, then attend."""
+        self.append_new(stream)
+        return self.extend(stream)
 
     def step(self, split: bool = True, stream=None):
         """One decode step: append the new tokens, attend, merge partitions."""

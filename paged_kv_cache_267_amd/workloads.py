@@ -191,9 +191,11 @@ def build(name: str, rng: np.random.Generator, seq_lens, *, num_q_heads: int,
     """
     L = np.asarray(seq_lens, dtype=np.int64)
     extend = q_lens is not None
-    n_new = np.asarray(q_lens, dtype=np.int64) if extend else np.ones_like(L)
-    assert n_new.shape == L.shape and (n_new >= 1).all() and (n_new <= L).all(), \
-        "every sequence brings 1..L new tokens"
+    # decode: one query row per sequence, whose token (if L > 0) is new
+    n_new = np.asarray(q_lens, dtype=np.int64) if extend else np.minimum(L, 1)
+    if extend:
+        assert n_new.shape == L.shape and (n_new >= 1).all() and (n_new <= L).all(), \
+            "every sequence brings 1..L new tokens"
     if shared_prefix:
         assert (L - n_new >= shared_prefix).all(), "new tokens lie after the shared prefix"
     S = int(L.shape[0])
@@ -238,7 +240,8 @@ def build(name: str, rng: np.random.Generator, seq_lens, *, num_q_heads: int,
     slots = (tables[tok_seq, tok_pos // bs].astype(np.int64) * bs + tok_pos % bs).astype(np.int32)
     is_new = tok_pos >= (L[tok_seq] - n_new[tok_seq])
 
-    q = rng.standard_normal((int(n_new.sum()), num_q_heads, D), dtype=np.float32)
+    q = rng.standard_normal((int(n_new.sum()) if extend else S, num_q_heads, D),
+                            dtype=np.float32)
     if zero_query:
         q[:] = 0.0
     kf = rng.standard_normal((T, Hkv, D), dtype=np.float32)

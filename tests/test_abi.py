@@ -80,6 +80,32 @@ def test_split_validation(kw, status):
     assert split(**kw) == status
 
 
+def ext(**kw):
+    args = dict(q=A, kc=A, vc=A, bt=A, sl=A, qsl=A, bs=16, scale=0.125, out=B, S=2, T=10, mq=8,
+                Hq=8, Hkv=2, D=128, mb=4, nb=8, win=0, qdt=1, kvdt=1, ks=1.0, vs=1.0,
+                stream=NULL)
+    args.update(kw)
+    return pa.lib().pa_extend(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), 1), (dict(qsl=NULL), 1), (dict(out=NULL), 1), (dict(sl=NULL), 1),
+    (dict(qdt=0, kvdt=0), 2), (dict(qdt=0, kvdt=1), 2), (dict(kvdt=0), 2), (dict(kvdt=9), 2),
+    (dict(S=-1), 3), (dict(T=-1), 3), (dict(mq=0), 3), (dict(mq=-1), 3), (dict(mq=1 << 21), 3),
+    (dict(Hq=6, Hkv=4), 3), (dict(win=-1), 3), (dict(scale=float("inf")), 3),
+    (dict(D=96), 4), (dict(bs=8), 4), (dict(Hq=64, Hkv=2), 4),
+    (dict(out=ODD), 7), (dict(q=ODD), 7),
+])
+def test_extend_validation(kw, status):
+    assert ext(**kw) == status
+
+
+def test_extend_empty_is_a_noop():
+    assert ext(S=0) == 0
+    assert ext(T=0, q=NULL, out=NULL, qsl=NULL) == 0
+    assert ext(T=0, qdt=0) == 2          # dtypes are checked first
+
+
 def test_reshape_and_cache_validation():
     L = pa.lib()
     ok = [A, A, A, A, A, 4, 2, 128, 16, 8, 1, NULL]

@@ -158,3 +158,139 @@ def test_extend_workloads_shapes():
         assert (wl.q_lens <= wl.seq_lens).all()
     wl = W.extend_config("chunked_prefill_bf16")
     assert wl.num_tokens == 8192 and wl.max_query_len == 1024
+
+
+# ---------------------------------------------------------------------------
+# GPU parity: the HIP kernel through the C ABI against the oracle
+
+TOL = {"bf16": (1e-2, 1e-3), "fp8_e4m3": (2e-2, 2e-3)}
+
+
+def half_ulp_bf16(x):
+    """Half the spacing of bf16 numbers at |x| (8 significand bits): the
+    error of the correctly rounded bf16 output itself."""
+    a = np.maximum(np.abs(x), 2.0 ** -126)
+    return 0.5 * np.exp2(np.floor(np.log2(a)) - 7)
+
+
+def _announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def _assert_close(got, ref, kv_dtype, what):
+    """The bf16 output is within the tolerance of the fp64 oracle once its own
+    rounding (half a bf16 ulp of the exact value) is set aside; mean as is."""
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    mx, mean = err_stats(got, ref)
+    tmax, tmean = TOL[kv_dtype]
+    excess = np.abs(got - ref) - half_ulp_bf16(ref)
+    at = np.unravel_index(int(np.argmax(excess)), got.shape)
+    mx_ex = float(max(excess.max(), 0.0))
+    print(f"    {what}: max abs {mx:.3e}, beyond bf16 rounding {mx_ex:.3e} (row {at[0]}, "
+          f"dim {at[1]}, ref {ref[at]:.4f}), mean abs {mean:.3e}", flush=True)
+    assert mx_ex <= tmax and mean <= tmean, f"{what}: max {mx_ex:.3e} mean {mean:.3e}"
+
+
+def _gpu_extend(wl):
+    from paged_kv_cache_267_amd.harness import DeviceWorkload
+    dw = DeviceWorkload(wl)
+    dw.fill_history()
+    dw.step_extend()
+    torch.cuda.synchronize()
+    return dw
+
+
+# lens / chunk lengths: a chunk that is the whole sequence, single tokens, a
+# chunk spanning several column blocks, chunks not a multiple of 16, and long
+# cached histories (several 32-key steps before the chunk)
+SMALL_LENS = [40, 1, 70, 300, 129, 33]
+SMALL_QLENS = [40, 1, 45, 100, 3, 17]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("kvdt", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bs", [16, 32, 64])
+@pytest.mark.parametrize("G", [1, 4, 16])
+@pytest.mark.parametrize("window", [0, 50])
+def test_extend_small_parity(kvdt, D, bs, G, window):
+    Hkv = 2 if G < 16 else 1
+    _announce(f"extend small kv={kvdt} D={D} bs={bs} G={G} W={window}")
+    wl = W.random_case(700 + D + bs + G + window, seq_lens=SMALL_LENS, q_lens=SMALL_QLENS,
+                       num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                       kv_dtype=kvdt, sliding_window=window, poison_out_of_window=window > 0)
+    kc, vc = oracle_caches(wl)
+    ref = oracle_extend(wl, kc, vc)
+    dw = _gpu_extend(wl)
+    _assert_close(dw.out_f64(), ref, kvdt, f"extend kv={kvdt} D={D} bs={bs} G={G} W={window}")
+
+
+def _sample_rows(wl, n, seed):
+    total = wl.num_tokens * wl.num_q_heads
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(total, size=min(n, total), replace=False).tolist())
+    # every head of the first and last token of the longest sequence
+    s = int(np.argmax(wl.seq_lens))
+    for t in (int(wl.query_start_loc[s]), int(wl.query_start_loc[s + 1]) - 1):
+        rows |= set(range(t * wl.num_q_heads, (t + 1) * wl.num_q_heads))
+    return np.array(sorted(rows), dtype=np.int32)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", W.EXTEND_NAMES)
+def test_extend_named_workload_parity(name):
+    _announce(f"extend workload {name}: generating")
+    wl = W.extend_config(name)
+    rows = _sample_rows(wl, 2048, seed=3)
+    kc, vc = oracle_caches(wl)
+    _announce(f"extend workload {name}: oracle on {rows.size} rows")
+    ref = oracle_extend(wl, kc, vc, rows=rows)
+    _announce(f"extend workload {name}: gpu")
+    dw = _gpu_extend(wl)
+    _assert_close(dw.out_f64()[rows], ref, wl.kv_dtype, f"extend {name}")
+
+
+@pytest.mark.gpu
+def test_extend_window_poison_variant():
+    _announce("extend fp8 window with out-of-window blocks pointing at a NaN block")
+    wl = W.extend_config("extend_fp8_window", poison_out_of_window=True)
+    rows = _sample_rows(wl, 1024, seed=4)
+    kc, vc = oracle_caches(wl)
+    ref = oracle_extend(wl, kc, vc, rows=rows)
+    dw = _gpu_extend(wl)
+    _assert_close(dw.out_f64()[rows], ref, wl.kv_dtype, "extend fp8 window poison")
+
+
+@pytest.mark.gpu
+def test_extend_edge_metadata():
+    """Chunks longer than their sequence (tokens at negative positions get
+    zero rows) and an empty chunk, checked against the oracle on the same
+    (modified) metadata."""
+    import paged_kv_cache_267_amd as pa
+    _announce("extend edge metadata")
+    wl = W.random_case(811, seq_lens=[50, 20, 64, 9], q_lens=[10, 20, 30, 9], num_q_heads=8,
+                       num_kv_heads=2, head_dim=128, block_size=16)
+    kc, vc = oracle_caches(wl)
+    dw = _gpu_extend(wl)
+    # sequence 1 keeps its rows but only 12 keys (8 tokens before position 0);
+    # sequence 2's chunk becomes empty, its 30 rows going to sequence 3 (39 tokens, 9 keys)
+    lens = np.array([50, 12, 64, 9], np.int32)
+    qsl = np.array([0, 10, 30, 30, 69], np.int32)
+    ref = oracle.extend(wl.query, kc, vc, wl.block_tables, lens, qsl, block_size=16,
+                        scale=wl.scale, num_kv_heads=2, q_dtype="bf16", kv_dtype="bf16")
+    out = torch.full_like(dw.out, float("nan"))
+    pa.pa_extend(dw.query, dw.key_cache, dw.value_cache, dw.block_tables,
+                 torch.from_numpy(lens).cuda(), torch.from_numpy(qsl).cuda(), block_size=16,
+                 scale=wl.scale, out=out, num_kv_heads=2, max_query_len=39)
+    torch.cuda.synchronize()
+    got = out.to(torch.float64).cpu().numpy().reshape(-1, 128)
+    _assert_close(got, ref, "bf16", "edge metadata")
+    zero_rows = ref.reshape(69, 8, 128)
+    assert not zero_rows[10:18].any() and not zero_rows[30:60].any()
+    assert not got.reshape(69, 8, 128)[10:18].any() and not got.reshape(69, 8, 128)[30:60].any()
+    # nothing to do: no sequences, or no tokens
+    pa.pa_extend(dw.query[:0], dw.key_cache, dw.value_cache, dw.block_tables,
+                 torch.zeros(4, dtype=torch.int32, device="cuda"),
+                 torch.zeros(5, dtype=torch.int32, device="cuda"), block_size=16,
+                 scale=wl.scale, out=out, num_kv_heads=2, max_query_len=0)
+    torch.cuda.synchronize()
