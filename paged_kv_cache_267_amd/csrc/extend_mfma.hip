@@ -15,29 +15,37 @@
 // of the MFMA tiles, whatever G is.
 //
 // Work.  One workgroup of 4 waves takes one (sequence, KV head, column
-// block); each wave owns CW = 16 * NCB consecutive columns and walks the keys
-// its columns need, 32 per step, loading K and V straight from the cache into
-// registers (a double buffer: the next step's loads are in flight while this
-// step computes).  The four waves read the same blocks, so the second and
-// later reads hit L2; column blocks of one (sequence, KV head) are dealt to
-// one XCD (workgroup j runs on XCD j % 8) so that they share its L2, and
-// (sequence, KV head) pairs are dealt round robin over the 8 XCDs.  Within a
-// pair the last column block (the most keys, causally) starts first.
+// block); each wave owns CW = 16 * NCB consecutive columns.  The workgroup
+// walks the keys its columns need, 32 per step, through a ring of NBUF LDS
+// stages: each wave moves a quarter of a step's K and V from the cache into
+// LDS with DMA loads (global_load_lds: no registers held while in flight),
+// NBUF - 1 steps ahead; one barrier per step publishes the stage and retires
+// the one read a step earlier.  Each wave then reads its MFMA operands from
+// LDS (one 16-byte read per lane and fragment, fragments laid out in lane
+// order, so the reads are conflict-free) and skips steps its own columns do
+// not need.  Column blocks of one (sequence, KV head) are dealt to one XCD
+// (workgroup j runs on XCD j % 8) so that they share its L2, pairs round
+// robin over the XCDs, the last column block of a pair (the most keys,
+// causally) first.
 //
 // Per step and column block of 16 columns (v_mfma_f32_16x16x32_bf16 for both
 // products, heads/tokens on N):
-//   S^T = K . Q^T   A = K (16 keys x 32 dims per k-step, the cache's 16-byte
-//                   groups as they lie), B = Q^T; two 16-key sub-tiles;
-//   O^T += V^T P^T  A = V^T (16 dims x 32 keys), B = P^T: lane (row r, col c)
-//                   holds keys 4r..4r+3 of both sub-tiles, which is exactly
-//                   what the two S^T fragments leave in that lane, so P never
-//                   moves between lanes.
-// Softmax state (running max, sum) is per column and lane-local; the max over
-// a fragment's 4 lane rows takes two lane swaps.  The running max is raised
-// lazily (rescale only when a column's max grows by more than 2^8), and it
-// starts at a large finite value so that a column whose keys are all masked
-// in a step keeps p = 0 and no NaN.  E4M3 codes become bf16 in registers
-// (exact); k_scale is folded into the score scale, v_scale applied at the end.
+//   S^T = K . Q^T   A = K (16 keys x 32 dims per k-step; lane (r, c) takes key
+//                   8(c/4) + c%4 (+4 for the second sub-tile) and the cache's
+//                   16-byte group r + 4k), B = Q^T;
+//   O^T += V^T P^T  A = V^T (16 dims x 32 keys), B = P^T: lane row r holds
+//                   keys 8r .. 8r+7 in both, which is what the two S^T
+//                   fragments leave in that lane, so P never moves between
+//                   lanes;
+//   l += 1 . P^T    one more MFMA with an all-ones A gives every column's sum
+//                   of the same bf16 weights P.V used, in every lane.
+// The running max is per column and lane-local (two lane swaps for the max
+// over a fragment's 4 lane rows), raised lazily: accumulators are rescaled
+// only when a column's max grows by more than 2^8.  It starts at a large
+// finite value, so a column whose keys are all masked in a step keeps p = 0
+// and no NaN.  The score scale (scale * k_scale * log2 e, positive) is folded
+// into the exponent's fused multiply-add.  E4M3 codes become bf16 in
+// registers (exact); v_scale is applied at the end.
 #include "dispatch.h"
 
 namespace pa {
@@ -45,10 +53,15 @@ namespace pa {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int EX_WAVES = 4;
+// Two workgroups per CU (two waves per SIMD): one wave's softmax issues
+// while the other's matrix products run.  Registers per wave <= 256.
+constexpr int EX_WG_PER_CU = 2;
 constexpr float EX_LAZY_LOG2 = 8.0f;
 constexpr float EX_M_FLOOR = -1.0e30f;
+constexpr uint32_t BF16_ONE_X2 = 0x3F803F80u;
 
 __device__ __forceinline__ float ex_colmax4(float x) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -56,64 +69,43 @@ __device__ __forceinline__ float ex_colmax4(float x) {
   auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ __forceinline__ float ex_colsum4(float x) {
-  const float y = swap_add32(x, x);
-  return swap_add16(y, y);
-}
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   return __builtin_bit_cast(bf16x8_t, (u32x4_t){a, b, c, d});
 }
 
-template <int KV, int D, int BS, int NCB>
-struct ExtendWave {
+// Wait until at most N vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; exp and lgkm counts left free).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int KV, int D, int BS, int NCB, int NBUF>
+struct ExtendTile {
   static constexpr int E = KvTraits<KV>::E;
   static constexpr int KS = D / 32;       // QK k-steps of 32 dims
   static constexpr int NB = D / 16;       // output dim blocks of 16
-  static constexpr int KL = D * E / 64;   // 16-byte K loads per lane per 16-key sub-tile
-  static constexpr int VW = E;            // V dwords per lane per dim block per sub-tile
+  static constexpr int KL = D * E / 64;   // 16-byte K granules per lane per 16-key sub-tile
   static constexpr int CW = 16 * NCB;     // columns per wave
-
-  struct Buf {
-    uint4 k[2][KL];
-    uint32_t v[2][NB][VW];
-  };
-
-  // Issue the loads of the 32 keys starting at key0 (a multiple of 32).
-  __device__ __forceinline__ static void load(Buf& b, const ExtendParams& p, const int32_t* row_bt,
-                                              int hk, int key0) {
-    const int lane = threadIdx.x & 63, r = lane >> 4, c = lane & 15;
-    const size_t tile = (size_t)D * BS * E;  // bytes of one (block, head) tile
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int key = key0 + 16 * h;
-      int blk = row_bt[min(key / BS, p.max_blocks - 1)];
-      blk = min(max(blk, 0), p.num_blocks - 1);
-      const size_t base = ((size_t)blk * p.num_kv_heads + hk) * tile;
-      const int sub = (key % BS) / 16;
-      const char* kp = p.kc + base + sub * 256 + (r * BS + c) * 16;
-      const char* vp = p.vc + base + (sub * 16 + c * BS + 4 * r) * E;
-#pragma unroll
-      for (int i = 0; i < KL; ++i) b.k[h][i] = load_nt16(kp + i * 4 * BS * 16);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const char* a = vp + (size_t)nb * 16 * BS * E;
-        if (VW == 2) {
-          const u32x2_t t = *(const u32x2_t*)a;
-          b.v[h][nb][0] = t.x;
-          b.v[h][nb][VW - 1] = t.y;
-        } else {
-          b.v[h][nb][0] = *(const uint32_t*)a;
-        }
-      }
-    }
-  }
+  // A step's fragments: 64 lanes x 16 bytes each, stored in lane order.
+  static constexpr int KF = 2 * KL;                       // K: (sub-tile, granule)
+  static constexpr int VF = KV == KV_BF16 ? NB : NB / 2;  // V: 8 keys of a dim (bf16) or
+                                                          //    16 keys of a dim (E4M3)
+  static constexpr int NF = KF + VF;
+  static constexpr int FW = NF / EX_WAVES;                // DMA loads per wave per step
+  static_assert(NF % EX_WAVES == 0, "every wave moves the same share of a step");
+  static_assert(KF == VF, "waves 0-1 move K, waves 2-3 move V");
+  static constexpr int STAGE = NF * 1024;
+  static constexpr int LDS_BYTES = NBUF * STAGE;
 };
 
-template <int KV, int D, int BS, int NCB>
-__global__ __launch_bounds__(EX_WAVES * 64) void extend_kernel(const ExtendParams p) {
-  using W = ExtendWave<KV, D, BS, NCB>;
-  constexpr int KS = W::KS, NB = W::NB, KL = W::KL, CW = W::CW;
+template <int KV, int D, int BS, int NCB, int NBUF>
+__global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(const ExtendParams p) {
+  using T = ExtendTile<KV, D, BS, NCB, NBUF>;
+  constexpr int KS = T::KS, NB = T::NB, KL = T::KL, CW = T::CW, KF = T::KF, FW = T::FW;
+  __shared__ __attribute__((aligned(1024))) char ring[T::LDS_BYTES];
   const int lane = threadIdx.x & 63, r = lane >> 4, c = lane & 15;
   const int wave = wave_id();
 
@@ -129,15 +121,30 @@ __global__ __launch_bounds__(EX_WAVES * 64) void extend_kernel(const ExtendParam
   const int q0 = min(max(p.qsl[s], 0), p.num_tokens);
   const int q1 = min(max(p.qsl[s + 1], q0), p.num_tokens);
   const int n = q1 - q0;
-  const int col0 = (cb * EX_WAVES + wave) * CW;
-  if (col0 >= (n << p.log2g)) return;  // no barriers below: a wave may leave alone
-  const int t_first = col0 >> p.log2g;
+  const int ncols = n << p.log2g;
+  const int wg_col0 = cb * EX_WAVES * CW;
+  if (wg_col0 >= ncols) return;  // the whole workgroup leaves before any barrier
+  const int W = p.window;
+  auto lo_of = [W](int hi) { return W > 0 ? max(0, hi - W) : 0; };
+
+  // keys of the workgroup (the union over its waves): first and last token
+  const int wg_hi_min = L - n + (wg_col0 >> p.log2g) + 1;
+  const int wg_hi_max = L - n + min(n - 1, (wg_col0 + EX_WAVES * CW - 1) >> p.log2g) + 1;
+  const int wg_klo = lo_of(max(wg_hi_min, 0));
+  const int wg_khi = max(wg_hi_max, 0);
+  const int kq0 = wg_klo >> 5;
+  const int nsteps = wg_khi > wg_klo ? ((wg_khi + 31) >> 5) - kq0 : 0;
+
+  // keys of this wave's columns (empty for a wave past the chunk)
+  const int col0 = wg_col0 + wave * CW;
+  const bool has_cols = col0 < ncols;
+  const int t_first = min(col0 >> p.log2g, n - 1);
   const int t_last = min(n - 1, (col0 + CW - 1) >> p.log2g);
-  const int hi_min = L - n + t_first + 1;  // exclusive key end of the first token
+  const int hi_min = L - n + t_first + 1;
   const int hi_max = L - n + t_last + 1;
-  const int lo_max = p.window > 0 ? max(0, hi_max - p.window) : 0;
-  const int klo = p.window > 0 ? max(0, max(hi_min, 0) - p.window) : 0;
-  const int khi = max(hi_max, 0);
+  const int lo_max = lo_of(hi_max);
+  const int klo = has_cols ? lo_of(max(hi_min, 0)) : 0;
+  const int khi = has_cols ? max(hi_max, 0) : 0;
   const int32_t* row_bt = p.block_tables + (size_t)s * p.max_blocks;
 
   // per lane: its column in each of the NCB column blocks
@@ -149,10 +156,9 @@ __global__ __launch_bounds__(EX_WAVES * 64) void extend_kernel(const ExtendParam
     const int t = cc >> p.log2g, g = cc & (G - 1);
     const bool valid = t < n && L - n + t >= 0;
     hi_c[j] = valid ? L - n + t + 1 : 0;
-    lo_c[j] = valid && p.window > 0 ? max(0, hi_c[j] - p.window) : 0;
+    lo_c[j] = valid ? lo_of(hi_c[j]) : 0;
     const int tq = min(t, n - 1);
-    const uint16_t* qrow =
-        p.q + ((size_t)(q0 + tq) * p.num_q_heads + hk * G + g) * D;
+    const uint16_t* qrow = p.q + ((size_t)(q0 + tq) * p.num_q_heads + hk * G + g) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int d0 = (KV == KV_BF16) ? 32 * ks + 8 * r : 16 * (r + 4 * (ks >> 1)) + 8 * (ks & 1);
@@ -162,135 +168,183 @@ __global__ __launch_bounds__(EX_WAVES * 64) void extend_kernel(const ExtendParam
     }
   }
 
-  f32x4_t acc[NCB][NB];
-  float m_ref[NCB], l_run[NCB];
+  f32x4_t acc[NCB][NB], accl[NCB];
+  float m_ref[NCB];
 #pragma unroll
   for (int j = 0; j < NCB; ++j) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[j][nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    accl[j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     m_ref[j] = EX_M_FLOOR;
-    l_run[j] = 0.f;
+  }
+  const bf16x8_t ones = as_bf16x8(BF16_ONE_X2, BF16_ONE_X2, BF16_ONE_X2, BF16_ONE_X2);
+  const float qk = p.qk_scale;
+  const size_t tile = (size_t)D * BS * T::E;  // bytes of one (block, head) tile
+
+  // DMA this wave's share of step `step` into stage `st`
+  auto fetch = [&](int step, int st) {
+    const int key0 = (kq0 + step) * 32;
+    const int bi = key0 / BS;
+    const int b0 = min(max(row_bt[min(bi, p.max_blocks - 1)], 0), p.num_blocks - 1);
+    int b1 = b0;
+    if (BS == 16) b1 = min(max(row_bt[min(bi + 1, p.max_blocks - 1)], 0), p.num_blocks - 1);
+    const size_t head = (size_t)hk * tile;
+    char* dst = ring + st * T::STAGE;
+    if (wave < 2) {  // K fragments (sub-tile h, granule i)
+      const int kk = 8 * (c >> 2) + (c & 3);           // key within the step (sub-tile 0)
+      const int blk = (BS == 16 && kk >= 16) ? b1 : b0;
+      const char* src = p.kc + (size_t)blk * p.num_kv_heads * tile + head +
+                        (r * BS + (key0 + kk) % BS) * 16;
+#pragma unroll
+      for (int jj = 0; jj < FW; ++jj) {
+        const int f = wave * FW + jj;
+        const int h = f / KL, i = f % KL;
+        __builtin_amdgcn_global_load_lds((const void*)(src + h * 64 + i * 4 * BS * 16),
+                                         (lds_void_t*)(dst + f * 1024), 16, 0, 0);
+      }
+    } else if (KV == KV_BF16) {  // V: dims 16v .. 16v+15, keys 8r .. 8r+7
+      const int blk = (BS == 16 && r >= 2) ? b1 : b0;
+      const char* src = p.vc + (size_t)blk * p.num_kv_heads * tile + head +
+                        (c * BS + (key0 + 8 * r) % BS) * 2;
+#pragma unroll
+      for (int jj = 0; jj < FW; ++jj) {
+        const int v = (wave - 2) * FW + jj;
+        __builtin_amdgcn_global_load_lds((const void*)(src + v * 16 * BS * 2),
+                                         (lds_void_t*)(dst + (KF + v) * 1024), 16, 0, 0);
+      }
+    } else {  // E4M3 V: dims 32v + 16(r/2) + c, keys 16(r%2) .. +15
+      const int blk = (BS == 16 && (r & 1)) ? b1 : b0;
+      const char* src = p.vc + (size_t)blk * p.num_kv_heads * tile + head +
+                        ((16 * (r >> 1) + c) * BS + (key0 + 16 * (r & 1)) % BS);
+#pragma unroll
+      for (int jj = 0; jj < FW; ++jj) {
+        const int v = (wave - 2) * FW + jj;
+        __builtin_amdgcn_global_load_lds((const void*)(src + v * 32 * BS),
+                                         (lds_void_t*)(dst + (KF + v) * 1024), 16, 0, 0);
+      }
+    }
+  };
+
+  if (nsteps > 0) {
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) fetch(min(i, nsteps - 1), i);
   }
 
-  const int kq0 = klo >> 5;
-  const int nsteps = khi > klo ? ((khi + 31) >> 5) - kq0 : 0;
+  for (int step = 0; step < nsteps; ++step) {
+    // this wave's share of `step` has landed; after the barrier everyone's
+    // has, and every wave is done with the stage read one step earlier
+    wait_vmcnt<(NBUF - 2) * FW>();
+    __syncthreads();
+    // refill that stage, NBUF - 1 steps ahead (past the end the last step is
+    // fetched again: the count of loads in flight stays fixed)
+    fetch(min(step + NBUF - 1, nsteps - 1), (step + NBUF - 1) % NBUF);
 
-  typename W::Buf buf[2];
-  if (nsteps > 0) W::load(buf[0], p, row_bt, hk, kq0 * 32);
+    const int key0 = (kq0 + step) * 32;
+    if (key0 + 32 <= klo || key0 >= khi) continue;  // no key of this wave's columns
+    const char* stage = ring + (step % NBUF) * T::STAGE;
 
-  for (int it = 0; it < nsteps; it += 2) {
+    // K operands of both sub-tiles (E4M3 -> bf16 in registers)
+    bf16x8_t kop[2][KS];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int step = it + u;
-      if (step >= nsteps) break;
-      // next step's loads (the last step reloads itself: loads stay unconditional)
-      W::load(buf[u ^ 1], p, row_bt, hk, (kq0 + min(step + 1, nsteps - 1)) * 32);
-      typename W::Buf& b = buf[u];
-      const int key0 = (kq0 + step) * 32;
-
-      // K operands of both sub-tiles (E4M3 -> bf16 in registers)
-      bf16x8_t kop[2][KS];
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < KL; ++i) {
-          const uint4 w = b.k[h][i];
-          if (KV == KV_BF16) {
-            kop[h][i] = as_bf16x8(w.x, w.y, w.z, w.w);
-          } else {
-            kop[h][2 * i] = as_bf16x8(fp8x2_to_bf16x2<false>(w.x), fp8x2_to_bf16x2<true>(w.x),
-                                      fp8x2_to_bf16x2<false>(w.y), fp8x2_to_bf16x2<true>(w.y));
-            kop[h][2 * i + 1] =
-                as_bf16x8(fp8x2_to_bf16x2<false>(w.z), fp8x2_to_bf16x2<true>(w.z),
-                          fp8x2_to_bf16x2<false>(w.w), fp8x2_to_bf16x2<true>(w.w));
-          }
+      for (int i = 0; i < KL; ++i) {
+        const u32x4_t w = *(const u32x4_t*)(stage + (h * KL + i) * 1024 + lane * 16);
+        if (KV == KV_BF16) {
+          kop[h][i] = as_bf16x8(w.x, w.y, w.z, w.w);
+        } else {
+          kop[h][2 * i] = as_bf16x8(fp8x2_to_bf16x2<false>(w.x), fp8x2_to_bf16x2<true>(w.x),
+                                    fp8x2_to_bf16x2<false>(w.y), fp8x2_to_bf16x2<true>(w.y));
+          kop[h][2 * i + 1] = as_bf16x8(fp8x2_to_bf16x2<false>(w.z), fp8x2_to_bf16x2<true>(w.z),
+                                        fp8x2_to_bf16x2<false>(w.w), fp8x2_to_bf16x2<true>(w.w));
         }
-      // V operands: k-slots 0..3 = keys 4r..4r+3 of sub-tile 0, 4..7 of sub-tile 1
-      uint32_t vq[NB][4];
+      }
+    // V operands: dword w holds keys 8r + 2w, 8r + 2w + 1 of dim 16nb + c
+    uint32_t vq[NB][4];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      if (KV == KV_BF16) {
+        const u32x4_t w = *(const u32x4_t*)(stage + (KF + nb) * 1024 + lane * 16);
+        vq[nb][0] = w.x;
+        vq[nb][1] = w.y;
+        vq[nb][2] = w.z;
+        vq[nb][3] = w.w;
+      } else {
+        const int rf = 2 * (nb & 1) + (r >> 1);  // the fetching lane row
+        const u32x2_t w = *(const u32x2_t*)(stage + (KF + (nb >> 1)) * 1024 +
+                                            (rf * 16 + c) * 16 + 8 * (r & 1));
+        vq[nb][0] = fp8x2_to_bf16x2<false>(w.x);
+        vq[nb][1] = fp8x2_to_bf16x2<true>(w.x);
+        vq[nb][2] = fp8x2_to_bf16x2<false>(w.y);
+        vq[nb][3] = fp8x2_to_bf16x2<true>(w.y);
+      }
+    }
+    // keys outside [klo, khi) may be unwritten or outside the window's
+    // blocks: zero their V so that p = 0 never meets a NaN
+    if (key0 < klo || key0 + 32 > khi) {
+      uint32_t vmask[4];
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const int kk = key0 + 8 * r + 2 * w2;
+        vmask[w2] = ((kk >= klo && kk < khi) ? 0xffffu : 0u) |
+                    ((kk + 1 >= klo && kk + 1 < khi) ? 0xffff0000u : 0u);
+      }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          if (KV == KV_BF16) {
-            vq[nb][2 * h] = b.v[h][nb][0];
-            vq[nb][2 * h + 1] = b.v[h][nb][W::VW - 1];
-          } else {
-            vq[nb][2 * h] = fp8x2_to_bf16x2<false>(b.v[h][nb][0]);
-            vq[nb][2 * h + 1] = fp8x2_to_bf16x2<true>(b.v[h][nb][0]);
-          }
-        }
-      // keys outside [klo, khi) may be unwritten or outside the window's
-      // blocks: zero their V so that p = 0 never meets a NaN
-      if (key0 < klo || key0 + 32 > khi) {
-        uint32_t vmask[4];
-#pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-          const int kk = key0 + 16 * (w2 >> 1) + 4 * r + 2 * (w2 & 1);
-          vmask[w2] = ((kk >= klo && kk < khi) ? 0xffffu : 0u) |
-                      ((kk + 1 >= klo && kk + 1 < khi) ? 0xffff0000u : 0u);
-        }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int w2 = 0; w2 < 4; ++w2) vq[nb][w2] &= vmask[w2];
-      }
-      const bool full = key0 >= lo_max && key0 + 32 <= hi_min && hi_min > 0;
+        for (int w2 = 0; w2 < 4; ++w2) vq[nb][w2] &= vmask[w2];
+    }
+    const bool full = key0 >= lo_max && key0 + 32 <= hi_min && hi_min > 0;
 
 #pragma unroll
-      for (int j = 0; j < NCB; ++j) {
-        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NCB; ++j) {
+      f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][ks], qop[j][ks], s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[1][ks], qop[j][ks], s1, 0, 0, 0);
-        }
-        float sc[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sc[i] = s0[i] * p.qk_scale;
-          sc[4 + i] = s1[i] * p.qk_scale;
-        }
-        if (!full) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int key = key0 + 16 * (i >> 2) + 4 * r + (i & 3);
-            if (!(key >= lo_c[j] && key < hi_c[j])) sc[i] = -INFINITY;
-          }
-        }
-        float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                         fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-        mx = ex_colmax4(mx);
-        if (__builtin_amdgcn_ballot_w64(mx > m_ref[j] + EX_LAZY_LOG2) != 0) {
-          const float m_new = fmaxf(m_ref[j], mx);
-          const float alpha = fast_exp2(m_ref[j] - m_new);
-          l_run[j] *= alpha;
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) acc[j][nb] *= alpha;
-          m_ref[j] = m_new;
-        }
-        float pr[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(sc[i] - m_ref[j]);
-        uint32_t pw[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pw[i] = pack_bf16x2(pr[2 * i], pr[2 * i + 1]);
-        // the sum takes the same bf16 weights the P.V product multiplies: the
-        // output stays a weighted mean of V rows, whatever the rounding of p
-        l_run[j] += ((bf16_lo(pw[0]) + bf16_hi(pw[0])) + (bf16_lo(pw[1]) + bf16_hi(pw[1]))) +
-                    ((bf16_lo(pw[2]) + bf16_hi(pw[2])) + (bf16_lo(pw[3]) + bf16_hi(pw[3])));
-        const bf16x8_t pop = as_bf16x8(pw[0], pw[1], pw[2], pw[3]);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              as_bf16x8(vq[nb][0], vq[nb][1], vq[nb][2], vq[nb][3]), pop, acc[j][nb], 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][ks], qop[j][ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[1][ks], qop[j][ks], s1, 0, 0, 0);
       }
+      // raw scores; slot i of lane row r is key key0 + 8r + i
+      float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int key = key0 + 8 * r + i;
+          if (!(key >= lo_c[j] && key < hi_c[j])) sc[i] = -INFINITY;
+        }
+      }
+      float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                       fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+      mx = ex_colmax4(mx) * qk;
+      if (__builtin_amdgcn_ballot_w64(mx > m_ref[j] + EX_LAZY_LOG2) != 0) {
+        const float m_new = fmaxf(m_ref[j], mx);
+        const float alpha = fast_exp2(m_ref[j] - m_new);
+        accl[j] *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[j][nb] *= alpha;
+        m_ref[j] = m_new;
+      }
+      uint32_t pw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pw[i] = pack_bf16x2(fast_exp2(__builtin_fmaf(sc[2 * i], qk, -m_ref[j])),
+                            fast_exp2(__builtin_fmaf(sc[2 * i + 1], qk, -m_ref[j])));
+      const bf16x8_t pop = as_bf16x8(pw[0], pw[1], pw[2], pw[3]);
+      accl[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop, accl[j], 0, 0, 0);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(vq[nb][0], vq[nb][1], vq[nb][2], vq[nb][3]), pop, acc[j][nb], 0, 0, 0);
     }
   }
+  // no DMA may still be writing this workgroup's LDS when it ends
+  wait_vmcnt<0>();
 
+  if (!has_cols) return;
   // normalise and store: lane (r, c) holds dims 16nb + 4r .. +3 of its column
 #pragma unroll
   for (int j = 0; j < NCB; ++j) {
-    const float l = ex_colsum4(l_run[j]);
+    const float l = accl[j][0];
     const float inv = l > 0.f ? p.v_scale / l : 0.f;
     const int cc = col0 + 16 * j + c;
     const int t = cc >> p.log2g, g = cc & (G - 1);
@@ -306,9 +360,10 @@ __global__ __launch_bounds__(EX_WAVES * 64) void extend_kernel(const ExtendParam
   }
 }
 
-// Column blocks of 16 per wave: enough registers for the accumulators, the
-// query operands and two steps of K/V in flight.
+// Column blocks of 16 per wave, and LDS stages in the ring (NBUF - 1 steps
+// in flight while one is computed).
 template <int D> constexpr int ex_ncb() { return D == 128 ? 2 : 4; }
+template <int D> constexpr int ex_nbuf() { return 3; }
 
 template <int KV, int D, int BS>
 hipError_t launch_ncb(const ExtendParams& p, hipStream_t stream) {
@@ -316,8 +371,8 @@ hipError_t launch_ncb(const ExtendParams& p, hipStream_t stream) {
   const long long grid = 8LL * ((p.pairs + 7) / 8) * p.cblocks;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((extend_kernel<KV, D, BS, NCB>), dim3((unsigned)grid), dim3(EX_WAVES * 64),
-                     0, stream, p);
+  hipLaunchKernelGGL((extend_kernel<KV, D, BS, NCB, ex_nbuf<D>()>), dim3((unsigned)grid),
+                     dim3(EX_WAVES * 64), 0, stream, p);
   return hipGetLastError();
 }
 
