@@ -11,6 +11,11 @@ bytes read per step / wall time per step).  `roofline` is the decode kernel's
 algorithmic bytes per launch / its average launch time (HIP events on the
 launch stream) against 8 TB/s.  `cpu_baseline` times the CPU oracle on the
 host cores over the same workload.
+
+With --extend NAME the step is the multi-token one instead: append every
+sequence's chunk of new tokens, then pa_extend; `value` is TFLOP/s of the
+attention (4 * head_dim flops per (query head, token, attended key)) and the
+roofline is the extend kernel against the bf16 dense matrix-core peak.
 """
 from __future__ import annotations
 
@@ -25,15 +30,27 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "paged decode attention: KV GB/s (% of MI355X HBM peak) + µs/call"
+EXTEND_METRIC = "paged extend attention: TFLOP/s (% of MI355X bf16 dense matrix peak)"
 DEFAULT_CFG = 2
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 
-def kernel_source_hash() -> str:
+# sources of the extend kernel; every other device source belongs to the decode path
+EXTEND_SOURCES = ("extend_mfma.hip", "common.h")
+
+
+def kernel_source_hash(family: str = "decode") -> str:
+    """Hash of the sources one kernel family is built from (recorded traffic
+    stays valid while they are unchanged)."""
     csrc = os.path.join(ROOT, "paged_kv_cache_267_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(csrc)):
+        if family == "extend" and f not in EXTEND_SOURCES:
+            continue
+        if family == "decode" and f in ("extend_mfma.hip", "block_manager.cpp"):
+            continue
         if f.endswith((".h", ".hip", ".cpp")):
             h.update(f.encode())
             h.update(open(os.path.join(csrc, f), "rb").read())
@@ -74,11 +91,13 @@ def load_traffic(kernel_hash: str, workload: str, mode: str):
     return r.get("bytes_per_launch")
 
 
-def record_traffic(fetch_csv: str, write_csv: str, key: str, khash: str, copy_mib: int) -> dict:
+def record_traffic(fetch_csv: str, write_csv: str, key: str, khash: str, copy_mib: int,
+                   kernel: str = "decode_persistent_kernel") -> dict:
     """HBM bytes per launch of the decode kernel from two rocprofv3 --pmc runs
     (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled so that the
     plain device copy of copy_mib MiB in the same run reads / writes exactly
-    its size.  Merged into profiles/decode_traffic.json under key."""
+    its size.  Merged into profiles/decode_traffic.json under key (kernel:
+    the name the counter rows carry)."""
     import csv
     import statistics
 
@@ -95,7 +114,7 @@ def record_traffic(fetch_csv: str, write_csv: str, key: str, khash: str, copy_mi
     copy_kib = copy_mib * 1024.0
     sf = copy_kib / max(pick(f, "copyBuffer"))
     sw = copy_kib / max(pick(w, "copyBuffer"))
-    df, dwr = pick(f, "decode_persistent_kernel"), pick(w, "decode_persistent_kernel")
+    df, dwr = pick(f, kernel), pick(w, kernel)
     fb = statistics.mean(df) * 1024 * sf
     wb = statistics.mean(dwr) * 1024 * sw
     rec = {"kernel_hash": khash, "bytes_per_launch": int(fb + wb), "fetch_bytes": int(fb),
@@ -162,6 +181,142 @@ def cpu_baseline(wl, budget_s: float):
                       f"{runs} run(s), {el:.1f} s, fp64, {round(el / runs * 1e3, 1)} ms/call"}
 
 
+def extend_flops(wl) -> int:
+    """Algorithmic flops of one extend launch: QK and PV, 2 * head_dim each,
+    per (query head, token, attended key)."""
+    return 4 * wl.head_dim * wl.num_q_heads * wl.attended_pairs()
+
+
+def extend_cpu_baseline(wl, budget_s: float):
+    """The oracle on a seeded sample of output rows, timed on the host cores
+    until about budget_s seconds of work; rate in the same flop count."""
+    import numpy as np
+    import oracle
+    from tests.helpers import oracle_caches
+    kc, vc = oracle_caches(wl)
+    rng = np.random.default_rng(7)
+    total = wl.num_tokens * wl.num_q_heads
+    qsl, L = wl.query_start_loc, wl.seq_lens.astype(np.int64)
+    seq_of = np.searchsorted(qsl, np.arange(wl.num_tokens), side="right") - 1
+    pos = L[seq_of] - (qsl[seq_of + 1] - qsl[seq_of]) + (np.arange(wl.num_tokens) - qsl[seq_of])
+    keys = pos + 1 if wl.sliding_window <= 0 else np.minimum(pos + 1, wl.sliding_window)
+    done_rows = flops = 0
+    t0 = time.perf_counter()
+    while True:
+        rows = np.sort(rng.choice(total, size=min(256, total), replace=False)).astype(np.int32)
+        oracle.extend(wl.query, kc, vc, wl.block_tables, wl.seq_lens, qsl,
+                      block_size=wl.block_size, scale=wl.scale, num_kv_heads=wl.num_kv_heads,
+                      q_dtype=wl.q_dtype, kv_dtype=wl.kv_dtype,
+                      sliding_window=wl.sliding_window, k_scale=wl.k_scale,
+                      v_scale=wl.v_scale, rows=rows)
+        done_rows += rows.size
+        flops += int(4 * wl.head_dim * keys[rows // wl.num_q_heads].sum())
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": round(flops / el / 1e12, 5), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{done_rows} random (token, head) rows of {total} in batches of 256, "
+                      f"{el:.1f} s, fp64"}
+
+
+def run_extend(args):
+    import numpy as np
+    import torch
+    from paged_kv_cache_267_amd import workloads as W
+    from paged_kv_cache_267_amd.harness import DeviceWorkload
+
+    wl = W.extend_config(args.extend)
+    dw = DeviceWorkload(wl)
+    dw.fill_history()
+    torch.cuda.synchronize()
+    print(f"[bench] {wl.name}: {wl.description}", file=sys.stderr, flush=True)
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        dw.step_extend()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        e = ev[k]
+        e[0].record(stream)
+        dw.append_new()
+        e[1].record(stream)
+        dw.extend()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    T = T_eager = time.perf_counter() - t0
+    graph = None
+    if not args.no_graph:
+        ref = dw.out.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            dw.step_extend()
+        for _ in range(3):
+            dw.out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(dw.out.view(torch.int16), ref.view(torch.int16)):
+                raise RuntimeError("graph replay differs from the eager step")
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        T = time.perf_counter() - t0
+        graph = {"ms_per_step": round(T / args.steps * 1e3, 4),
+                 "check": "3 replays bit-identical to the eager step output"}
+        del g
+    ms_step = T / args.steps * 1e3
+    t_app = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
+    t_ext = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+    fl = extend_flops(wl)
+    value = fl / (ms_step * 1e-3) / 1e12
+    achieved = fl / (t_ext * 1e-6) / 1e12
+    G = wl.num_q_heads // wl.num_kv_heads
+    rec = {
+        "metric": EXTEND_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"{wl.q_dtype} q / {wl.kv_dtype} kv, bf16 matrix products, fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description,
+                   "global_batch": wl.num_seqs, "query_tokens": wl.num_tokens,
+                   "max_query_len": wl.max_query_len,
+                   "seq_len_mean": float(wl.seq_lens.mean()), "parallelism": "single GPU"},
+        "step_breakdown_us": {"reshape_and_cache": round(t_app, 2), "extend": round(t_ext, 2),
+                              "eager_wall_per_step": round(T_eager / args.steps * 1e6, 2),
+                              "wall_per_step": round(ms_step * 1e3, 2)},
+        "step_timing": "hip graph replay of the step" if graph else "eager launches",
+        "graph": graph,
+        "flops_per_step": fl,
+        "kv_bytes_per_step": wl.kv_bytes(),
+        "unique_kv_bytes_per_step": int(wl.unique_kv_bytes()),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": load_traffic(kernel_source_hash("extend"), wl.name, "extend"),
+                     "kernel": f"extend_kernel<{1 if wl.kv_dtype == 'bf16' else 2}, "
+                               f"{wl.head_dim}, {wl.block_size}, ...>, G={G}",
+                     "algorithmic_flops_per_launch": fl, "avg_launch_us": round(t_ext, 2),
+                     "kernel_hash": kernel_source_hash("extend")},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle sample) ...", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = extend_cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,12 +344,27 @@ def main():
                          "(0: skip)")
     ap.add_argument("--kernel", choices=["auto", "valu", "mfma"], default="auto",
                     help="decode kernel family (auto: matrix cores for GQA groups >= 8)")
+    ap.add_argument("--extend", default=None,
+                    help="time the multi-token step on this extend workload instead "
+                         "(chunked_prefill_bf16, prefix_extend_bf16, extend_fp8_window)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode path has no multi-GPU leg "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.extend:
+        if args.record_traffic:
+            assert args.calibrate_copy_mib > 0, "--calibrate-copy-mib must name the copy size"
+            from paged_kv_cache_267_amd import workloads as W
+            rec = record_traffic(*args.record_traffic, f"{args.extend}/extend",
+                                 kernel_source_hash("extend"), args.calibrate_copy_mib,
+                                 kernel="extend_kernel")
+            print(json.dumps({f"{args.extend}/extend": rec}))
+            return
+        run_extend(args)
+        return
 
     import numpy as np
     import torch
