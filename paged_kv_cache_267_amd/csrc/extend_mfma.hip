@@ -55,9 +55,10 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// Two workgroups of 4 waves per CU (two waves per SIMD, from different
+// workgroups): one wave's softmax issues while the other's matrix products
+// run.  Registers per wave <= 256.
 constexpr int EX_WAVES = 4;
-// Two workgroups per CU (two waves per SIMD): one wave's softmax issues
-// while the other's matrix products run.  Registers per wave <= 256.
 constexpr int EX_WG_PER_CU = 2;
 constexpr float EX_LAZY_LOG2 = 8.0f;
 constexpr float EX_M_FLOOR = -1.0e30f;
@@ -82,6 +83,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Workgroup barrier for the LDS ring: this wave's LDS reads are complete
+// (lgkmcnt 0) and every wave has arrived.  No memory fence: a fence would
+// also wait for the DMA loads still in flight for later steps (they count
+// as outstanding LDS writes), which must stay in flight across the barrier;
+// each wave waits for its own DMA of the step with an exact vmcnt instead.
+// The empty asm statements keep the compiler from moving LDS accesses
+// across the barrier.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4));  // lgkmcnt(0), vmcnt/expcnt free
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int KV, int D, int BS, int NCB, int NBUF>
 struct ExtendTile {
   static constexpr int E = KvTraits<KV>::E;
@@ -94,9 +109,11 @@ struct ExtendTile {
   static constexpr int VF = KV == KV_BF16 ? NB : NB / 2;  // V: 8 keys of a dim (bf16) or
                                                           //    16 keys of a dim (E4M3)
   static constexpr int NF = KF + VF;
-  static constexpr int FW = NF / EX_WAVES;                // DMA loads per wave per step
-  static_assert(NF % EX_WAVES == 0, "every wave moves the same share of a step");
-  static_assert(KF == VF, "waves 0-1 move K, waves 2-3 move V");
+  // DMA loads per moving wave per step; the first NFW waves move a step
+  // (K first, then V), the others only compute
+  static constexpr int FW = NF >= EX_WAVES ? NF / EX_WAVES : 1;
+  static constexpr int NFW = NF / FW;
+  static_assert(NF % FW == 0 && KF % FW == 0 && NFW <= EX_WAVES, "whole fragments per wave");
   static constexpr int STAGE = NF * 1024;
   static constexpr int LDS_BYTES = NBUF * STAGE;
 };
@@ -105,6 +122,7 @@ template <int KV, int D, int BS, int NCB, int NBUF>
 __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(const ExtendParams p) {
   using T = ExtendTile<KV, D, BS, NCB, NBUF>;
   constexpr int KS = T::KS, NB = T::NB, KL = T::KL, CW = T::CW, KF = T::KF, FW = T::FW;
+  constexpr int NFW = T::NFW;
   __shared__ __attribute__((aligned(1024))) char ring[T::LDS_BYTES];
   const int lane = threadIdx.x & 63, r = lane >> 4, c = lane & 15;
   const int wave = wave_id();
@@ -181,50 +199,63 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
   const float qk = p.qk_scale;
   const size_t tile = (size_t)D * BS * T::E;  // bytes of one (block, head) tile
 
-  // DMA this wave's share of step `step` into stage `st`
-  auto fetch = [&](int step, int st) {
-    const int key0 = (kq0 + step) * 32;
-    const int bi = key0 / BS;
-    const int b0 = min(max(row_bt[min(bi, p.max_blocks - 1)], 0), p.num_blocks - 1);
-    int b1 = b0;
-    if (BS == 16) b1 = min(max(row_bt[min(bi + 1, p.max_blocks - 1)], 0), p.num_blocks - 1);
-    const size_t head = (size_t)hk * tile;
-    char* dst = ring + st * T::STAGE;
-    if (wave < 2) {  // K fragments (sub-tile h, granule i)
-      const int kk = 8 * (c >> 2) + (c & 3);           // key within the step (sub-tile 0)
-      const int blk = (BS == 16 && kk >= 16) ? b1 : b0;
-      const char* src = p.kc + (size_t)blk * p.num_kv_heads * tile + head +
-                        (r * BS + (key0 + kk) % BS) * 16;
-#pragma unroll
-      for (int jj = 0; jj < FW; ++jj) {
-        const int f = wave * FW + jj;
-        const int h = f / KL, i = f % KL;
-        __builtin_amdgcn_global_load_lds((const void*)(src + h * 64 + i * 4 * BS * 16),
-                                         (lds_void_t*)(dst + f * 1024), 16, 0, 0);
-      }
-    } else if (KV == KV_BF16) {  // V: dims 16v .. 16v+15, keys 8r .. 8r+7
-      const int blk = (BS == 16 && r >= 2) ? b1 : b0;
-      const char* src = p.vc + (size_t)blk * p.num_kv_heads * tile + head +
-                        (c * BS + (key0 + 8 * r) % BS) * 2;
-#pragma unroll
-      for (int jj = 0; jj < FW; ++jj) {
-        const int v = (wave - 2) * FW + jj;
-        __builtin_amdgcn_global_load_lds((const void*)(src + v * 16 * BS * 2),
-                                         (lds_void_t*)(dst + (KF + v) * 1024), 16, 0, 0);
-      }
-    } else {  // E4M3 V: dims 32v + 16(r/2) + c, keys 16(r%2) .. +15
-      const int blk = (BS == 16 && (r & 1)) ? b1 : b0;
-      const char* src = p.vc + (size_t)blk * p.num_kv_heads * tile + head +
-                        ((16 * (r >> 1) + c) * BS + (key0 + 16 * (r & 1)) % BS);
-#pragma unroll
-      for (int jj = 0; jj < FW; ++jj) {
-        const int v = (wave - 2) * FW + jj;
-        __builtin_amdgcn_global_load_lds((const void*)(src + v * 32 * BS),
-                                         (lds_void_t*)(dst + (KF + v) * 1024), 16, 0, 0);
-      }
+  // Block-table entries of a 64-block window, one per lane: a step's block
+  // ids come from a lane read, not from memory, so no step waits on a load
+  // issued after the DMA loads still in flight (vmcnt retires in order).
+  // Moving the window (every 64 blocks) waits for them once.
+  int tb_base = -64, tb = 0;
+  auto block_id = [&](int bi) -> int {
+    const int base = bi & ~63;
+    if (base != tb_base) {
+      tb_base = base;
+      tb = row_bt[min(base + lane, p.max_blocks - 1)];
     }
+    const int b = __builtin_amdgcn_readlane(tb, bi - base);
+    return min(max(b, 0), p.num_blocks - 1);
   };
 
+  // This wave's fragments of a step are slots wave*FW .. wave*FW+FW-1 of the
+  // stage (K fragments first, then V).  Per lane: the step's base address,
+  // plus a per-fragment offset.
+  const bool moves_k = wave * FW < KF;
+  auto step_src = [&](int step) -> const char* {
+    const int key0 = (kq0 + step) * 32;
+    const int bi = min(key0 / BS, p.max_blocks - 1);
+    const int b0 = block_id(bi);
+    int b1 = b0;
+    if (BS == 16) b1 = block_id(min(bi + 1, p.max_blocks - 1));
+    const size_t head = (size_t)hk * tile;
+    if (moves_k) {  // K: lane (r, c) takes key 8(c/4) + c%4 (+4), group r (+4i)
+      const int kk = 8 * (c >> 2) + (c & 3);
+      const int blk = (BS == 16 && kk >= 16) ? b1 : b0;
+      return p.kc + (size_t)blk * p.num_kv_heads * tile + head + (r * BS + (key0 + kk) % BS) * 16;
+    }
+    if (KV == KV_BF16) {  // V: dims 16v + c, keys 8r .. 8r+7
+      const int blk = (BS == 16 && r >= 2) ? b1 : b0;
+      return p.vc + (size_t)blk * p.num_kv_heads * tile + head + (c * BS + (key0 + 8 * r) % BS) * 2;
+    }
+    // E4M3 V: dims 32v + 16(r/2) + c, keys 16(r%2) .. +15
+    const int blk = (BS == 16 && (r & 1)) ? b1 : b0;
+    return p.vc + (size_t)blk * p.num_kv_heads * tile + head +
+           ((16 * (r >> 1) + c) * BS + (key0 + 16 * (r & 1)) % BS);
+  };
+  auto frag_off = [&](int jj) -> int {
+    const int f = wave * FW + jj;
+    if (moves_k) return (f / KL) * 64 + (f % KL) * 4 * BS * 16;
+    const int v = f - KF;
+    return KV == KV_BF16 ? v * 16 * BS * 2 : v * 32 * BS;
+  };
+  auto slot = [&](int st, int jj) -> char* { return ring + st * T::STAGE + (wave * FW + jj) * 1024; };
+
+  // DMA this wave's share of step `step` into stage `st`
+  auto fetch = [&](int step, int st) {
+    if (wave >= NFW) return;
+    const char* src = step_src(step);
+#pragma unroll
+    for (int jj = 0; jj < FW; ++jj)
+      __builtin_amdgcn_global_load_lds((const void*)(src + frag_off(jj)),
+                                       (lds_void_t*)slot(st, jj), 16, 0, 0);
+  };
   if (nsteps > 0) {
 #pragma unroll
     for (int i = 0; i < NBUF - 1; ++i) fetch(min(i, nsteps - 1), i);
@@ -232,15 +263,20 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
 
   for (int step = 0; step < nsteps; ++step) {
     // this wave's share of `step` has landed; after the barrier everyone's
-    // has, and every wave is done with the stage read one step earlier
+    // has, and every wave is done with the stage read one step earlier.  The
+    // barrier orders LDS only: a full __syncthreads would also drain the
+    // DMA loads of the later steps and serialise loading with computing.
     wait_vmcnt<(NBUF - 2) * FW>();
-    __syncthreads();
-    // refill that stage, NBUF - 1 steps ahead (past the end the last step is
-    // fetched again: the count of loads in flight stays fixed)
-    fetch(min(step + NBUF - 1, nsteps - 1), (step + NBUF - 1) % NBUF);
+    ring_barrier();
+    // the stage to refill NBUF - 1 steps ahead (past the end the last step
+    // is fetched again: the count of loads in flight stays fixed)
+    const int ahead = min(step + NBUF - 1, nsteps - 1), ahead_st = (step + NBUF - 1) % NBUF;
 
     const int key0 = (kq0 + step) * 32;
-    if (key0 + 32 <= klo || key0 >= khi) continue;  // no key of this wave's columns
+    if (key0 + 32 <= klo || key0 >= khi) {  // no key of this wave's columns
+      fetch(ahead, ahead_st);
+      continue;
+    }
     const char* stage = ring + (step % NBUF) * T::STAGE;
 
     // K operands of both sub-tiles (E4M3 -> bf16 in registers)
@@ -259,6 +295,25 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
                                         fp8x2_to_bf16x2<false>(w.w), fp8x2_to_bf16x2<true>(w.w));
         }
       }
+    const bool full = key0 >= lo_max && key0 + 32 <= hi_min && hi_min > 0;
+
+    // scores of every column block first: the V reads below overlap them
+    f32x4_t sacc[NCB][2];
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) {
+      sacc[j][0] = sacc[j][1] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sacc[j][0] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][ks], qop[j][ks], sacc[j][0], 0, 0, 0);
+        sacc[j][1] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[1][ks], qop[j][ks], sacc[j][1], 0, 0, 0);
+      }
+    }
+
+    // refill while the score products run
+    fetch(ahead, ahead_st);
+
     // V operands: dword w holds keys 8r + 2w, 8r + 2w + 1 of dim 16nb + c
     uint32_t vq[NB][4];
 #pragma unroll
@@ -294,16 +349,10 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
 #pragma unroll
         for (int w2 = 0; w2 < 4; ++w2) vq[nb][w2] &= vmask[w2];
     }
-    const bool full = key0 >= lo_max && key0 + 32 <= hi_min && hi_min > 0;
-
+    bf16x8_t pop[NCB];
 #pragma unroll
     for (int j = 0; j < NCB; ++j) {
-      f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][ks], qop[j][ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[1][ks], qop[j][ks], s1, 0, 0, 0);
-      }
+      const f32x4_t s0 = sacc[j][0], s1 = sacc[j][1];
       // raw scores; slot i of lane row r is key key0 + 8r + i
       float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
       if (!full) {
@@ -329,12 +378,16 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
       for (int i = 0; i < 4; ++i)
         pw[i] = pack_bf16x2(fast_exp2(__builtin_fmaf(sc[2 * i], qk, -m_ref[j])),
                             fast_exp2(__builtin_fmaf(sc[2 * i + 1], qk, -m_ref[j])));
-      const bf16x8_t pop = as_bf16x8(pw[0], pw[1], pw[2], pw[3]);
-      accl[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop, accl[j], 0, 0, 0);
+      pop[j] = as_bf16x8(pw[0], pw[1], pw[2], pw[3]);
+    }
+    // then every column block's P.V: one run of independent matrix products
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) {
+      accl[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop[j], accl[j], 0, 0, 0);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            as_bf16x8(vq[nb][0], vq[nb][1], vq[nb][2], vq[nb][3]), pop, acc[j][nb], 0, 0, 0);
+            as_bf16x8(vq[nb][0], vq[nb][1], vq[nb][2], vq[nb][3]), pop[j], acc[j][nb], 0, 0, 0);
     }
   }
   // no DMA may still be writing this workgroup's LDS when it ends
