@@ -37,8 +37,14 @@ DEFAULT_CFG = 2
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 
-# sources of the extend kernel; every other device source belongs to the decode path
-EXTEND_SOURCES = ("extend_mfma.hip", "common.h")
+def family_sources(family: str, names) -> list:
+    """The device sources a kernel family is built from: the extend kernel's
+    file, or the decode driver, its tiles and instances; both include
+    common.h and are launched through dispatch.*"""
+    shared = ("common.h", "dispatch.h", "dispatch.cpp")
+    if family == "extend":
+        return [f for f in names if f == "extend_mfma.hip" or f in shared]
+    return [f for f in names if f.startswith(("decode_", "tile_")) or f in shared]
 
 
 def kernel_source_hash(family: str = "decode") -> str:
@@ -46,11 +52,7 @@ def kernel_source_hash(family: str = "decode") -> str:
     stays valid while they are unchanged)."""
     csrc = os.path.join(ROOT, "paged_kv_cache_267_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
-        if family == "extend" and f not in EXTEND_SOURCES:
-            continue
-        if family == "decode" and f in ("extend_mfma.hip", "block_manager.cpp"):
-            continue
+    for f in sorted(family_sources(family, os.listdir(csrc))):
         if f.endswith((".h", ".hip", ".cpp")):
             h.update(f.encode())
             h.update(open(os.path.join(csrc, f), "rb").read())

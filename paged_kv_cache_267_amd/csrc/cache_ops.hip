@@ -21,9 +21,12 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long total = (long long)num_tokens * Hkv * groups;
   if (gid >= total) return;
-  const int grp = (int)(gid % groups);
-  const int h = (int)((gid / groups) % Hkv);
-  const int t = (int)(gid / ((long long)groups * Hkv));
+  // token fastest: neighbouring lanes take neighbouring tokens, whose slots
+  // are usually neighbours in one block (a chunk of new tokens), so the
+  // 16-byte K groups and the V elements of a row land side by side
+  const int t = (int)(gid % num_tokens);
+  const int grp = (int)((gid / num_tokens) % groups);
+  const int h = (int)(gid / ((long long)num_tokens * groups));
   const int slot = slots[t];
   if (slot < 0 || (long long)slot >= num_slots) return;
   const int b = slot / bs, o = slot % bs;
@@ -77,9 +80,12 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long total = (long long)num_tokens * Hkv * groups;
   if (gid >= total) return;
-  const int grp = (int)(gid % groups);
-  const int h = (int)((gid / groups) % Hkv);
-  const int t = (int)(gid / ((long long)groups * Hkv));
+  // token fastest: neighbouring lanes take neighbouring tokens, whose slots
+  // are usually neighbours in one block (a chunk of new tokens), so the
+  // 16-byte K groups and the V elements of a row land side by side
+  const int t = (int)(gid % num_tokens);
+  const int grp = (int)((gid / num_tokens) % groups);
+  const int h = (int)(gid / ((long long)num_tokens * groups));
   const int slot = slots[t];
   if (slot < 0 || (long long)slot >= num_slots) return;
   const int b = slot / bs, o = slot % bs;
