@@ -194,6 +194,7 @@ int pa_decode_split(const void* query, const void* key_cache, const void* value_
  *                   to num_tokens.
  * max_query_len     >= every n_s (the launch is sized by it); 1 .. 2^20 when
  *                   num_tokens > 0.
+ * num_tokens        <= 2^26.
  * scale, k_scale    finite and > 0 (PA_ERR_SHAPE otherwise).
  * Caches, block tables, seq_lens, head_dim, block_size, group sizes, scales,
  * alignment and the clamping of out-of-range device data are as for

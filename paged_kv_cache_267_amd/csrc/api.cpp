@@ -195,6 +195,7 @@ int pa_extend(const void* query, const void* key_cache, const void* value_cache,
   if (!query_start_loc || !out) return PA_ERR_NULL;
   if (!(scale > 0.f) || !(k_scale > 0.f)) return PA_ERR_SHAPE;  // the max is taken on raw scores
   if (num_tokens < 0 || max_query_len < 0 || max_query_len > (1 << 20)) return PA_ERR_SHAPE;
+  if (num_tokens > (1 << 26)) return PA_ERR_SHAPE;  // column indices (token x head) stay in int
   if (num_tokens > 0 && max_query_len == 0) return PA_ERR_SHAPE;
   if ((long long)num_tokens * num_q_heads * head_dim >= (1ll << 40)) return PA_ERR_SHAPE;
   if (!aligned16(out)) return PA_ERR_ALIGN;

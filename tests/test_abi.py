@@ -92,6 +92,7 @@ def ext(**kw):
     (dict(q=NULL), 1), (dict(qsl=NULL), 1), (dict(out=NULL), 1), (dict(sl=NULL), 1),
     (dict(qdt=0, kvdt=0), 2), (dict(qdt=0, kvdt=1), 2), (dict(kvdt=0), 2), (dict(kvdt=9), 2),
     (dict(S=-1), 3), (dict(T=-1), 3), (dict(mq=0), 3), (dict(mq=-1), 3), (dict(mq=1 << 21), 3),
+    (dict(T=(1 << 26) + 1), 3),
     (dict(Hq=6, Hkv=4), 3), (dict(win=-1), 3), (dict(scale=float("inf")), 3),
     (dict(scale=0.0), 3), (dict(scale=-0.1), 3), (dict(ks=0.0), 3),
     (dict(D=96), 4), (dict(bs=8), 4), (dict(Hq=64, Hkv=2), 4),
