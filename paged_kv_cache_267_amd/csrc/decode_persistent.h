@@ -214,24 +214,25 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
     }
     for (int i = tid; i < CHUNKS * NBK; i += NTH) (&sm.u.srt.cnt[0][0])[i] = 0;
     __syncthreads();
-    // entry e sits in chunk e / 64 (one wave's lanes); its rank among the
-    // chunk's entries of its class comes from one ballot per class present
+    // entry e sits in chunk e / 64 (one wave's lanes); the lanes holding its
+    // class are found bit-sliced (one ballot per bit of the 6-bit class), so
+    // its rank among the chunk's entries of that class costs a fixed 7 ballots
     int mine[SR], cls[SR], wr[SR];
 #pragma unroll
     for (int r = 0; r < SR; ++r) {
       const int e = tid + r * NTH, c = wave + r * (NTH / 64);
       const bool valid = e < NPART;
       mine[r] = valid ? sm.plist[e] : 0;
-      cls[r] = valid ? sm.u.srt.cls[e] : NBK;
-      wr[r] = 0;
-      uint64_t todo = __builtin_amdgcn_ballot_w64(valid);
-      while (todo) {
-        const int k = __builtin_amdgcn_readlane(cls[r], (int)__builtin_ctzll(todo));
-        const uint64_t m = __builtin_amdgcn_ballot_w64(cls[r] == k);
-        if (cls[r] == k) wr[r] = __builtin_popcountll(m & ((1ull << lane) - 1));
-        if (lane == 0) sm.u.srt.cnt[c][k] = __builtin_popcountll(m);
-        todo &= ~m;
+      cls[r] = valid ? sm.u.srt.cls[e] : 0;
+      uint64_t same = __builtin_amdgcn_ballot_w64(valid);
+#pragma unroll
+      for (int bit = 0; bit < 6; ++bit) {
+        const bool set = (cls[r] >> bit) & 1;
+        const uint64_t bm = __builtin_amdgcn_ballot_w64(valid && set);
+        same &= set ? bm : ~bm;
       }
+      wr[r] = __builtin_popcountll(same & ((1ull << lane) - 1));
+      if (valid && wr[r] == 0) sm.u.srt.cnt[c][cls[r]] = __builtin_popcountll(same);
     }
     __syncthreads();
     // class starts (exclusive scan over classes of the chunk totals), then each
@@ -315,39 +316,35 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
   }
   auto list_index = [&](int m) -> int { return deal(m_lo + m); };
 
-  // k-th segment of the list -> (sequence, partition).  A workgroup asks for
-  // increasing k, so the search for a full partition's (or, unsorted, a
-  // partial segment's) sequence resumes where the previous one stopped.
-  int hint_f = 0, hint_p = 0;
+  // k-th segment of the list -> (sequence, partition), in each lane on its
+  // own: a sorted partial segment is read from the ordered list; otherwise a
+  // binary search over the exclusive prefix counts finds the sequence.
   auto seg_of = [&](int k, int& si, int& pp) {
     const bool full = k < F;
     const int kk = full ? k : k - F;
     if (!full && sorted) {
-      const int e = uniform(sm.plist[kk]);
+      const int e = sm.plist[kk];
       si = e >> 20;
       pp = e & 0xfffff;
       return;
     }
     const int32_t* pre = full ? sm.fpre : sm.ppre;
-    si = full ? hint_f : hint_p;
-    for (;;) {
-      const int i = si + lane;
-      const int v = i < S ? pre[i + 1] : 0x7fffffff;
-      const uint64_t hit = __builtin_amdgcn_ballot_w64(v > kk);
-      if (hit) { si += __builtin_ctzll(hit); break; }
-      si += 64;
+    int lo = 0, hi = S;   // pre[lo] <= kk < pre[hi]; the sequence is the last such lo
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pre[mid] <= kk) lo = mid;
+      else hi = mid;
     }
-    if (full) hint_f = si;
-    else hint_p = si;
-    const int L = uniform(sm.lens[si]);
+    si = lo;
+    const int L = sm.lens[si];
     int nf, np, f0;
     counts(L, nf, np, f0);
-    const int r = kk - uniform(pre[si]);
+    const int r = kk - pre[si];
     if (full) {
       pp = f0 + r;
     } else {
-      const int lo = (p.window > 0 && L > p.window) ? L - p.window : 0;
-      const int p_lo = P ? lo / P : 0, p_hi = P ? (L + P - 1) / P : 1;
+      const int lo_t = (p.window > 0 && L > p.window) ? L - p.window : 0;
+      const int p_lo = P ? lo_t / P : 0, p_hi = P ? (L + P - 1) / P : 1;
       int t0, t1;
       seg_range(L, p_lo, t0, t1);
       const bool first_partial = P == 0 || t1 - t0 != P;
@@ -421,50 +418,63 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
   int bm = 0, bst = -1;  // next batch starts at segment bm, sub-tile bst (-1: its start)
 
   while (bm < M) {
-    // ---- batch plan (wave 0, scalar) -----------------------------------------------
+    // ---- batch plan (wave 0; lane i plans slot i) -------------------------------------
+    // Slot i takes list entry bm + i (slot 0 resumes a carried segment at
+    // sub-tile bst).  Slots are taken in order while their blocks fit in the
+    // staged table; a first slot that alone overflows it takes what fits and
+    // the segment continues in the next batch.
     if (wave == 0) {
-      int m = bm, st_start = bst, cnt = 0, used = 0;
-      int next_m = M, next_st = -1;
-      while (m < M && cnt < SLOTS) {
-        int si, pp;
+      // the lane index comes from an opaque instruction here, so the compiler
+      // keeps this per-lane work inside the planner instead of hoisting
+      // loop-invariant per-lane values into registers held by the main loop
+      int pl;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(pl));
+      const int m = bm + pl;
+      const bool have = pl < SLOTS && m < M;
+      int st_hi = 0, a = 0, nb = 0;
+      if (have) {
+        int si, pp, t0, t1;
         seg_of(list_index(m), si, pp);
-        const int L = uniform(sm.lens[si]);
-        int t0, t1;
-        seg_range(L, pp, t0, t1);
-        const int st_lo = t0 >> 4, st_hi = t0 < t1 ? (t1 + 15) >> 4 : st_lo;
-        const int a = st_start >= 0 ? st_start : st_lo;
-        // this batch's share of the segment: sub-tiles [a, b), blocks
-        // [a / SPB, ceil(b / SPB)); a segment that does not fit starts a new batch,
-        // unless it is the first slot (then it takes what fits and continues)
-        int b = st_hi;
-        const int room = PD_TBL - used;
-        if (b > a && (b + SPB - 1) / SPB - a / SPB > room) {
-          if (cnt > 0) { next_m = m; next_st = st_start; break; }
-          b = (a / SPB + room) * SPB;
-        }
-        const int nblk = b > a ? (b + SPB - 1) / SPB - a / SPB : 0;
-        // table entries to stage: their index into block_tables for now
-        const int row0 = (s0 + si) * p.max_blocks + a / SPB;
-        for (int i = lane; i < nblk; i += 64) sm.tbl[used + i] = row0 + i;
-        if (lane == 0) {
-          SegMeta& md = sm.meta[cnt];
-          md.s = si; md.p = pp; md.t0 = t0; md.t1 = t1;
-          md.st_a = a; md.st_b = b; md.tbl = used; md.fin = b >= st_hi ? 1 : 0;
-        }
-        used += nblk;
-        ++cnt;
-        if (b < st_hi) { next_m = m; next_st = b; break; }
-        ++m;
-        st_start = -1;
-        next_m = m;
-        next_st = -1;
+        seg_range(sm.lens[si], pp, t0, t1);
+        const int st_lo = t0 >> 4;
+        st_hi = t0 < t1 ? (t1 + 15) >> 4 : st_lo;
+        a = (pl == 0 && bst >= 0) ? bst : st_lo;
+        nb = st_hi > a ? (st_hi + SPB - 1) / SPB - a / SPB : 0;
+        SegMeta& md = sm.meta[pl];   // rest of the slot's record once the batch is cut
+        md.s = si; md.p = pp; md.t0 = t0; md.t1 = t1; md.st_a = a;
       }
-      if (lane == 0) {
+      int incl = nb;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (pl >= off) incl += y;
+      }
+      const uint64_t stop = __builtin_amdgcn_ballot_w64(!have || incl > PD_TBL);
+      const int f = (int)__builtin_ctzll(stop);     // lanes >= SLOTS never have a slot
+      const bool trunc = f == 0;                    // the first slot alone overflows the table
+      const int cnt = trunc ? 1 : f;
+      int b = st_hi;
+      if (trunc) {
+        b = (a / SPB + PD_TBL) * SPB;
+        nb = PD_TBL;
+        incl = PD_TBL;
+      }
+      if (pl < cnt) {
+        SegMeta& md = sm.meta[pl];
+        md.st_b = b; md.tbl = incl - nb; md.fin = b >= st_hi ? 1 : 0;
+      }
+      // table entries to stage: their index into block_tables for now
+      for (int c = 0; c < cnt; ++c) {
+        const int n = __builtin_amdgcn_readlane(nb, c), at = __builtin_amdgcn_readlane(incl, c) - n;
+        const int r0 = (s0 + uniform(sm.meta[c].s)) * p.max_blocks + uniform(sm.meta[c].st_a) / SPB;
+        for (int i = pl; i < n; i += 64) sm.tbl[at + i] = r0 + i;
+      }
+      if (pl == 0) {
         sm.bcount = cnt;
-        sm.bnext_m = next_m;
-        sm.bnext_st = next_st;
-        sm.bused = used;
+        sm.bnext_m = trunc ? bm : bm + cnt;
+        sm.bnext_st = trunc ? b : -1;
       }
+      if (pl == cnt - 1) sm.bused = incl;
     }
     __syncthreads();
     const int nslot = uniform(sm.bcount);

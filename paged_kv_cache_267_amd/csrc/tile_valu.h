@@ -49,7 +49,7 @@ struct ValuTile {
   // register buffers (sub-tile bytes per lane: f32 256, bf16 128, E4M3 64)
   static constexpr int NBUF = KV == KV_F32 ? 2 : KV == KV_FP8 ? 4 : 3;
   static constexpr int QROWB = D * EQ + 16;                // staged query row bytes
-  static constexpr int QBYTES = 16384;
+  static constexpr int QBYTES = KV == KV_FP8 ? 32768 : 16384;
   static constexpr int NPAR = 2;
   static_assert(C % 4 == 0 && VPL >= 1, "head_dim too small for this element size");
 
