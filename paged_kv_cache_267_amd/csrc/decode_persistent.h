@@ -75,7 +75,7 @@ struct SegMeta {
 template <class T>
 struct PdGeom {
   static constexpr int SLOTS_RAW = T::QBYTES / (T::G * T::QROWB);
-  static constexpr int SLOTS = SLOTS_RAW < 32 ? SLOTS_RAW : 32;  // segments per batch
+  static constexpr int SLOTS = SLOTS_RAW < 64 ? SLOTS_RAW : 64;  // segments per batch (one per lane of the planner)
   static_assert(SLOTS >= 1, "query staging too small");
 };
 
@@ -89,16 +89,20 @@ struct PdSmem {
   int32_t tbl[PD_TBL];               // staged block ids of the batch
   alignas(16) uint8_t q[SLOTS][G][T::QROWB];   // staged query rows of the batch
   SegMeta meta[SLOTS];
-  int32_t bcount, bnext_m, bnext_st, bused, scan[2][PD_WAVES];
-  int32_t arrived[T::NPAR];          // deposits into each merge area (4 per use)
-  int32_t done[T::NPAR];             // quarter merges out of each area (4 per use)
-  typename T::WaveLds wl[PD_WAVES];  // per-wave scratch of the tile computation
+  int32_t bcount, bnext_m, bnext_st, bused, scan[2][PD_WAVES * T::HALVES];
+  int32_t next_slot;                 // slots of the batch claimed so far
+  int32_t carry_half;                // half holding a segment that continues into the next batch
+  int32_t hslot[T::HALVES][SLOTS + 1];   // slot of each half's k-th segment (-1 open, -2 none)
+  int32_t hlock[T::HALVES][SLOTS + 1];   // claim of that entry taken
+  int32_t arrived[T::HALVES][T::NPAR];   // deposits into each merge area (4 per use)
+  int32_t done[T::HALVES][T::NPAR];      // quarter merges out of each area (4 per use)
+  typename T::WaveLds wl[PD_WAVES * T::HALVES];  // per-wave scratch of the tile computation
   union alignas(16) {
     struct {
       float m[PD_WAVES][G];
       float l[PD_WAVES][G];
       float acc[PD_WAVES][G][D + 4];  // rows padded: no bank conflicts
-    } area[T::NPAR];
+    } area[T::HALVES][T::NPAR];
     struct {                          // ordering of the partial segments, before any merge
       int32_t cls[PD_SORT_MAX];
       int32_t cnt[PD_SORT_MAX / 64][PD_SIZE_CLASSES];
@@ -107,11 +111,12 @@ struct PdSmem {
 };
 
 template <class T>
-__global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_kernel(DecodeParams p) {
   constexpr int D = T::D, BS = T::BS, G = T::G, E = T::E, EQ = T::EQ;
   constexpr int SPB = BS / 16;
   constexpr size_t TILE_BYTES = (size_t)D * BS * E;
-  constexpr int NTH = 64 * PD_WAVES;
+  constexpr int HV = T::HALVES;         // independent 4-wave halves per workgroup
+  constexpr int NTH = 64 * PD_WAVES * HV;
   constexpr int SLOTS = PdGeom<T>::SLOTS;
   constexpr int NPAR = T::NPAR;
   static_assert(G <= 16, "at most 16 query heads per KV head");
@@ -119,6 +124,7 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
   __shared__ PdSmem<T> sm;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int h = wave / PD_WAVES, hw = wave % PD_WAVES;   // half, wave within the half
   const int H = p.num_kv_heads, Hq = p.num_q_heads;
   const int hk = blockIdx.x % H;
   const int j = blockIdx.x / H, J = gridDim.x / H;
@@ -260,10 +266,11 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
         sm.plist[sm.u.srt.cnt[wave + r * (NTH / 64)][cls[r]] + wr[r]] = mine[r];
     __syncthreads();
   }
-  if (tid < NPAR) {
-    sm.arrived[tid] = 0;
-    sm.done[tid] = 0;
+  if (tid < HV * NPAR) {
+    (&sm.arrived[0][0])[tid] = 0;
+    (&sm.done[0][0])[tid] = 0;
   }
+  if (tid == 0) sm.carry_half = 0;
   __syncthreads();
   const int total = F + NPART;
   // The list is dealt in serpentine order: round r gives dealing slot d entry
@@ -373,18 +380,18 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
     while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target)
       __builtin_amdgcn_s_sleep(1);
   };
-  // Merge of the 4 waves' states of a finished segment, done by quarters: wave
-  // w combines (in wave order) and writes outputs [w, w+1) * G*D/4 of the
-  // segment's G x D block.
+  // Merge of the 4 states a half's waves left for a finished segment, done by
+  // quarters: wave w of the half combines (in wave order) and writes outputs
+  // [w, w+1) * G*D/4 of the segment's G x D block.
   auto merge_quarter = [&]() {
     if (pend_s < 0) return;
     constexpr int QN = G * D / PD_WAVES;
     const int par = pend_par;
-    spin_until(&sm.arrived[par], PD_WAVES * (pend_gen + 1));
-    auto& ar = sm.u.area[par];
+    spin_until(&sm.arrived[h][par], PD_WAVES * (pend_gen + 1));
+    auto& ar = sm.u.area[h][par];
 #pragma unroll
     for (int i0 = 0; i0 < QN; i0 += 64) {
-      const int e = wave * QN + i0 + lane;
+      const int e = hw * QN + i0 + lane;
       if (QN % 64 == 0 || i0 + lane < QN) {
         const int g = e / D, d = e % D;
         float mx = -INFINITY;
@@ -411,7 +418,7 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
       }
     }
     if (lane == 0)
-      __hip_atomic_fetch_add(&sm.done[par], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_fetch_add(&sm.done[h][par], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     pend_s = -1;
   };
 
@@ -431,7 +438,7 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
       asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(pl));
       const int m = bm + pl;
       const bool have = pl < SLOTS && m < M;
-      int st_hi = 0, a = 0, nb = 0;
+      int st_hi = 0, a = 0, nb = 0, row0 = 0;
       if (have) {
         int si, pp, t0, t1;
         seg_of(list_index(m), si, pp);
@@ -442,6 +449,7 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
         nb = st_hi > a ? (st_hi + SPB - 1) / SPB - a / SPB : 0;
         SegMeta& md = sm.meta[pl];   // rest of the slot's record once the batch is cut
         md.s = si; md.p = pp; md.t0 = t0; md.t1 = t1; md.st_a = a;
+        row0 = (s0 + si) * p.max_blocks + a / SPB;   // block_tables index of the first block
       }
       int incl = nb;
 #pragma unroll
@@ -466,10 +474,19 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
       // table entries to stage: their index into block_tables for now
       for (int c = 0; c < cnt; ++c) {
         const int n = __builtin_amdgcn_readlane(nb, c), at = __builtin_amdgcn_readlane(incl, c) - n;
-        const int r0 = (s0 + uniform(sm.meta[c].s)) * p.max_blocks + uniform(sm.meta[c].st_a) / SPB;
+        const int r0 = __builtin_amdgcn_readlane(row0, c);
         for (int i = pl; i < n; i += 64) sm.tbl[at + i] = r0 + i;
       }
+      // claims of the batch's slots: open, except that a segment carried over
+      // from the last batch stays with the half that holds its running state
+      for (int i = pl; i < HV * (SLOTS + 1); i += 64) {
+        (&sm.hslot[0][0])[i] = -1;
+        (&sm.hlock[0][0])[i] = 0;
+      }
       if (pl == 0) {
+        const int ch = sm.carry_half;
+        if (bst >= 0) { sm.hslot[ch][0] = 0; sm.hlock[ch][0] = 1; }
+        sm.next_slot = bst >= 0 ? 1 : 0;
         sm.bcount = cnt;
         sm.bnext_m = trunc ? bm : bm + cnt;
         sm.bnext_st = trunc ? b : -1;
@@ -489,7 +506,7 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
       constexpr int QV = D * EQ / 16;
       constexpr int TPT = PD_TBL / NTH;                              // table entries per thread
       constexpr int QPT = (SLOTS * G * QV + NTH - 1) / NTH;          // query pieces per thread
-      static_assert(TPT == 8 && QPT <= 8, "staging registers");
+      static_assert(TPT >= 1 && TPT <= 8 && QPT <= 8, "staging registers");
       const int ntbl = uniform(sm.bused), nq = nslot * G * QV;
       // held in vector registers (not arrays, which the compiler would place
       // in scratch memory)
@@ -529,29 +546,58 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
     }
     __syncthreads();
 
-    // ---- tile stream of this wave over the batch's slots -------------------------------
-    // Sub-tiles are dealt to the waves round-robin from the segment's first
-    // sub-tile; first_st(c) is this wave's first sub-tile >= st_a in slot c.
+    // ---- tile stream of this wave over its half's slots --------------------------------
+    // Each half takes the batch's slots one at a time, in list order, as it
+    // reaches them (the first of its waves to need its k-th slot claims the
+    // next unclaimed one), so a faster half simply takes more of them.  Within
+    // a slot the half's 4 waves take sub-tiles round-robin from the segment's
+    // first sub-tile; first_st(c) is this wave's first sub-tile >= st_a.
     auto first_st = [&](int c) -> int {
       const int st_lo = uniform(sm.meta[c].t0) >> 4, a = uniform(sm.meta[c].st_a);
-      return a + (((wave - (a - st_lo)) % PD_WAVES) + PD_WAVES) % PD_WAVES;
+      return a + (((hw - (a - st_lo)) % PD_WAVES) + PD_WAVES) % PD_WAVES;
     };
-    int cs = 0, cst = nslot > 0 ? first_st(0) : 0;   // load cursor: slot, sub-tile
-    auto settle = [&]() {        // move the cursor to a slot with a tile left
-      while (cs < nslot && cst >= uniform(sm.meta[cs].st_b)) {
-        ++cs;
-        if (cs < nslot) cst = first_st(cs);
+    auto claim = [&](int k) -> int {   // slot of this half's k-th segment, or -2
+      int v = -1;
+      if (lane == 0) {
+        v = __hip_atomic_load(&sm.hslot[h][k], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (v == -1) {
+          if (__hip_atomic_exchange(&sm.hlock[h][k], 1, __ATOMIC_ACQ_REL,
+                                    __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
+            const int c = __hip_atomic_fetch_add(&sm.next_slot, 1, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+            v = c < nslot ? c : -2;
+            if (v >= 0 && !sm.meta[v].fin) sm.carry_half = h;
+            __hip_atomic_store(&sm.hslot[h][k], v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+          } else {   // another wave of the half is claiming it right now
+            do {
+              __builtin_amdgcn_s_sleep(1);
+              v = __hip_atomic_load(&sm.hslot[h][k], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            } while (v == -1);
+          }
+        }
       }
+      return __builtin_amdgcn_readfirstlane(v);
+    };
+    // load cursor: the half's k-th slot lk, which is batch slot cs (-2: none
+    // left; then kend = lk slots were the half's), and its sub-tile cst
+    int lk = 0, cs = claim(0), cst = cs >= 0 ? first_st(cs) : 0, kend = 1 << 30;
+    auto settle = [&]() {        // move the cursor to a slot with a tile left
+      while (cs >= 0 && cst >= uniform(sm.meta[cs].st_b)) {
+        ++lk;
+        cs = claim(lk);
+        if (cs >= 0) cst = first_st(cs);
+      }
+      if (cs < 0) kend = lk;
     };
     settle();
 
     auto load_tile = [&](Buf& b) {
       int phys = 0, st = 0;
-      if (cs < nslot) {
+      if (cs >= 0) {
         st = cst;
         const int blk = st / SPB - uniform(sm.meta[cs].st_a) / SPB;
         phys = uniform(sm.tbl[uniform(sm.meta[cs].tbl) + blk]);
-        b.slot = cs;
+        b.slot = (lk << 8) | cs;   // the half's index of the slot, and the batch slot
         b.st = st;
         cst += PD_WAVES;
         settle();
@@ -574,11 +620,11 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
       merge_quarter();
       const int par = uses % NPAR, gen = uses / NPAR;
       ++uses;
-      spin_until(&sm.done[par], PD_WAVES * gen);   // the area's previous use is merged
-      auto& ar = sm.u.area[par];
-      tile.deposit(ar.m[wave], ar.l[wave], ar.acc[wave]);
+      spin_until(&sm.done[h][par], PD_WAVES * gen);   // the area's previous use is merged
+      auto& ar = sm.u.area[h][par];
+      tile.deposit(ar.m[hw], ar.l[hw], ar.acc[hw]);
       if (lane == 0)
-        __hip_atomic_fetch_add(&sm.arrived[par], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_add(&sm.arrived[h][par], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       tile.reset();
       pend_s = s0 + uniform(sm.meta[c].s);
       pend_pp = uniform(sm.meta[c].p);
@@ -588,20 +634,22 @@ __global__ __launch_bounds__(64 * PD_WAVES) void decode_persistent_kernel(Decode
 
     // ---- main loop: NBUF buffers, NBUF - 1 tiles in flight --------------------------------
     constexpr int NBUF = T::NBUF;
-    int cur = 0;                 // slot whose state the wave holds
-    set_query(0);
+    int ck = 0;                  // the half's index of the slot whose state the wave holds
+    auto slot_of = [&](int k) -> int { return uniform(sm.hslot[h][k]); };   // claimed already
+    if (kend > 0) set_query(slot_of(0));
 #pragma unroll
     for (int i = 0; i + 1 < NBUF; ++i) load_tile(bufs[i]);
     auto step = [&](Buf& cb, Buf& spare) -> bool {
       load_tile(spare);
-      const int target = cb.slot < 0 ? nslot : cb.slot;
-      while (cur < target) {     // every slot is visited, in order, by every wave
-        finish_slot(cur);
-        ++cur;
-        if (cur < nslot) set_query(cur);
+      const int target = cb.slot < 0 ? kend : (cb.slot >> 8);
+      while (ck < target) {      // every slot of the half is visited, in order, by its waves
+        finish_slot(slot_of(ck));
+        ++ck;
+        if (ck < kend) set_query(slot_of(ck));
       }
       if (cb.slot < 0) return false;
-      tile.compute(cb, uniform(sm.meta[cb.slot].t0), uniform(sm.meta[cb.slot].t1), p.qk_scale,
+      const int c = cb.slot & 255;
+      tile.compute(cb, uniform(sm.meta[c].t0), uniform(sm.meta[c].t1), p.qk_scale,
                    sm.wl[wave]);
       return true;
     };
@@ -626,7 +674,8 @@ hipError_t launch_decode_persistent(const DecodeParams& p0, hipStream_t stream) 
   if (per_cu < 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_persistent_kernel<T>,
-                                                     64 * PD_WAVES, 0) != hipSuccess || n < 1)
+                                                     64 * PD_WAVES * T::HALVES, 0) != hipSuccess ||
+        n < 1)
       n = 1;
     per_cu = n;
   }
@@ -646,7 +695,7 @@ hipError_t launch_decode_persistent(const DecodeParams& p0, hipStream_t stream) 
     // the first J*H/2 workgroups are dispatched one per CU, the rest pair up with them
     p.pairs = (per_cu == 2 && J * H == 2LL * cus) ? 1 : 0;
     hipLaunchKernelGGL((decode_persistent_kernel<T>), dim3((unsigned)(J * H)),
-                       dim3(64 * PD_WAVES), 0, stream, p);
+                       dim3(64 * PD_WAVES * T::HALVES), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

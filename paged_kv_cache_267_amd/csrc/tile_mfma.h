@@ -58,8 +58,9 @@ struct MfmaTile {
   // (E4M3 sub-tiles are half the bytes, so twice as many)
   static constexpr int NBUF = KV == KV_FP8 ? 5 : 3;
   static constexpr int QROWB = (D + 8) * 2;    // staged query row (padded: no bank conflicts)
-  static constexpr int QBYTES = G == 8 ? 24576 : G > 8 ? 8192 : 16384;
+  static constexpr int QBYTES = G == 8 ? 57344 : G > 8 ? 32768 : 65536;
   static constexpr int NPAR = G <= 8 ? 2 : 1;  // merge areas that fit next to the rest
+  static constexpr int HALVES = 2;             // two 4-wave halves per workgroup
 
   struct Buf {
     uint4 k[KL];

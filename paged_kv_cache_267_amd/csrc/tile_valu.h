@@ -49,8 +49,11 @@ struct ValuTile {
   // register buffers (sub-tile bytes per lane: f32 256, bf16 128, E4M3 64)
   static constexpr int NBUF = KV == KV_F32 ? 2 : KV == KV_FP8 ? 4 : 3;
   static constexpr int QROWB = D * EQ + 16;                // staged query row bytes
-  static constexpr int QBYTES = KV == KV_FP8 ? 32768 : 16384;
   static constexpr int NPAR = 2;
+  // two 4-wave halves per workgroup where two waves per SIMD fit in registers
+  static constexpr int HALVES = (G <= 4 && !(KV == KV_F32 && D == 128 && G > 1)) ? 2 : 1;
+  // staged query bytes: E4M3 segments are cheap to stream, so a batch holds more of them
+  static constexpr int QBYTES = (KV == KV_FP8 && HALVES == 2) ? 65536 : 16384;
   static_assert(C % 4 == 0 && VPL >= 1, "head_dim too small for this element size");
 
   struct Buf {

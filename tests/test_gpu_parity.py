@@ -202,6 +202,24 @@ def test_decode_small_parity(kvdt, D, bs, G, split):
         assert np.all(got[L == 0] == 0.0)   # L = 0 rows are exact zeros
 
 
+@pytest.mark.parametrize("kvdt,G", [("bf16", 4), ("bf16", 8), ("fp8_e4m3", 4)])
+def test_decode_segments_longer_than_staged_table(kvdt, G):
+    """Unsplit segments of 2200-2500 blocks (more than one batch's staged table)
+    carry their running state into the next batch, next to short sequences
+    that the workgroup's halves take in between."""
+    lens = [40000, 5, 300, 35200, 17, 900, 2200, 1]
+    wl = W.random_case(4242 + G, seq_lens=lens, num_q_heads=2 * G, num_kv_heads=2,
+                       head_dim=128, block_size=16, kv_dtype=kvdt, partition_size=1024)
+    kc, vc = oracle_caches(wl)
+    ref = oracle_decode(wl, kc, vc)
+    for k in kernels(kvdt, G):
+        for split in (False, True):
+            announce(f"long segments {kvdt} G{G} split={split} kernel={k}")
+            with pa.decode_kernel(k):
+                got = gpu_run(wl, split=split).out_f64()
+            assert_close(got, ref, kvdt, f"long segments split={split} ({k})")
+
+
 @pytest.mark.parametrize("kvdt", ["bf16", "fp8_e4m3"])
 def test_split_partials_and_lse(kvdt):
     import torch
