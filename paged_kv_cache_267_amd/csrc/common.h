@@ -154,6 +154,30 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 // Index of the calling wave in its workgroup, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return uniform((int)(threadIdx.x >> 6)); }
 
+// Flags and counters in LDS shared by the waves of a workgroup: relaxed LDS
+// atomics with fences restricted to LDS.  A plain acquire / release at
+// workgroup scope would also wait for every outstanding global load of the
+// wave (s_waitcnt vmcnt(0)), draining the K/V tiles it has in flight.
+__device__ __forceinline__ int lds_load_acquire(const int32_t* p) {
+  const int v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  return v;
+}
+__device__ __forceinline__ void lds_store_release(int32_t* p, int v) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ int lds_add_release(int32_t* p, int v) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ int lds_exchange_acq_rel(int32_t* p, int v) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  const int r = __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  return r;
+}
+
 // Workgroup barrier ordering LDS only: the calling waves' outstanding global
 // loads stay in flight across it (a full __syncthreads would drain them).
 __device__ __forceinline__ void lds_barrier() {

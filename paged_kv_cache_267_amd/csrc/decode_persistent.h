@@ -377,7 +377,7 @@ __global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_k
   int pend_s = -1, pend_pp = 0, pend_par = 0, pend_gen = 0;
 
   auto spin_until = [&](const int32_t* ctr, int target) {
-    while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target)
+    while (lds_load_acquire(ctr) < target)
       __builtin_amdgcn_s_sleep(1);
   };
   // Merge of the 4 states a half's waves left for a finished segment, done by
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_k
       }
     }
     if (lane == 0)
-      __hip_atomic_fetch_add(&sm.done[h][par], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      lds_add_release(&sm.done[h][par], 1);
     pend_s = -1;
   };
 
@@ -559,19 +559,18 @@ __global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_k
     auto claim = [&](int k) -> int {   // slot of this half's k-th segment, or -2
       int v = -1;
       if (lane == 0) {
-        v = __hip_atomic_load(&sm.hslot[h][k], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        v = lds_load_acquire(&sm.hslot[h][k]);
         if (v == -1) {
-          if (__hip_atomic_exchange(&sm.hlock[h][k], 1, __ATOMIC_ACQ_REL,
-                                    __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
+          if (lds_exchange_acq_rel(&sm.hlock[h][k], 1) == 0) {
             const int c = __hip_atomic_fetch_add(&sm.next_slot, 1, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_WORKGROUP);
             v = c < nslot ? c : -2;
             if (v >= 0 && !sm.meta[v].fin) sm.carry_half = h;
-            __hip_atomic_store(&sm.hslot[h][k], v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            lds_store_release(&sm.hslot[h][k], v);
           } else {   // another wave of the half is claiming it right now
             do {
               __builtin_amdgcn_s_sleep(1);
-              v = __hip_atomic_load(&sm.hslot[h][k], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+              v = lds_load_acquire(&sm.hslot[h][k]);
             } while (v == -1);
           }
         }
@@ -597,7 +596,7 @@ __global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_k
         st = cst;
         const int blk = st / SPB - uniform(sm.meta[cs].st_a) / SPB;
         phys = uniform(sm.tbl[uniform(sm.meta[cs].tbl) + blk]);
-        b.slot = (lk << 8) | cs;   // the half's index of the slot, and the batch slot
+        b.slot = cs;
         b.st = st;
         cst += PD_WAVES;
         settle();
@@ -624,7 +623,7 @@ __global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_k
       auto& ar = sm.u.area[h][par];
       tile.deposit(ar.m[hw], ar.l[hw], ar.acc[hw]);
       if (lane == 0)
-        __hip_atomic_fetch_add(&sm.arrived[h][par], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        lds_add_release(&sm.arrived[h][par], 1);
       tile.reset();
       pend_s = s0 + uniform(sm.meta[c].s);
       pend_pp = uniform(sm.meta[c].p);
@@ -634,22 +633,31 @@ __global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_k
 
     // ---- main loop: NBUF buffers, NBUF - 1 tiles in flight --------------------------------
     constexpr int NBUF = T::NBUF;
-    int ck = 0;                  // the half's index of the slot whose state the wave holds
+    // A half's slots are claimed in increasing batch order, so the slot whose
+    // state the wave holds (the half's ck-th, batch slot cslot) is behind a
+    // tile's slot exactly when cslot is smaller.
     auto slot_of = [&](int k) -> int { return uniform(sm.hslot[h][k]); };   // claimed already
-    if (kend > 0) set_query(slot_of(0));
+    int ck = 0, cslot = kend > 0 ? slot_of(0) : (1 << 30);
+    if (kend > 0) set_query(cslot);
 #pragma unroll
     for (int i = 0; i + 1 < NBUF; ++i) load_tile(bufs[i]);
     auto step = [&](Buf& cb, Buf& spare) -> bool {
       load_tile(spare);
-      const int target = cb.slot < 0 ? kend : (cb.slot >> 8);
-      while (ck < target) {      // every slot of the half is visited, in order, by its waves
-        finish_slot(slot_of(ck));
-        ++ck;
-        if (ck < kend) set_query(slot_of(ck));
+      if (cb.slot < 0) {         // past the half's last tile: finish its remaining slots
+        while (ck < kend) {
+          finish_slot(cslot);
+          ++ck;
+          if (ck < kend) cslot = slot_of(ck);
+        }
+        return false;
       }
-      if (cb.slot < 0) return false;
-      const int c = cb.slot & 255;
-      tile.compute(cb, uniform(sm.meta[c].t0), uniform(sm.meta[c].t1), p.qk_scale,
+      while (cslot < cb.slot) {  // every slot of the half is visited, in order, by its waves
+        finish_slot(cslot);
+        ++ck;
+        cslot = slot_of(ck);
+        set_query(cslot);
+      }
+      tile.compute(cb, uniform(sm.meta[cb.slot].t0), uniform(sm.meta[cb.slot].t1), p.qk_scale,
                    sm.wl[wave]);
       return true;
     };
