@@ -20,28 +20,35 @@
 // unsplit), largest first by a stable counting sort over size classes.  Each
 // workgroup builds the list from the lengths in LDS, so all agree on it.
 //
+// Halves.  Where two waves per SIMD fit in registers, a workgroup is 8 waves,
+// one per CU, made of two independent halves of 4 waves; otherwise it is one
+// half.  The halves take the batch's segments one at a time, in list order, as
+// they reach them (a claim through LDS atomics), so a half that the CU serves
+// faster takes more of them and both finish together.
+//
 // Memory pipeline.  The workgroup walks its segments in batches.  For a batch
 // it stages, in LDS, the block-table entries of every block the batch touches
 // and the query rows of its segments (blocks wholly before the window are
 // never listed); after that the only global loads until the batch ends are
 // K/V sub-tiles (16 tokens of one block).  Each wave streams its sub-tiles
-// (the 4 waves take a segment's sub-tiles round-robin) NBUF - 1 tiles ahead
-// across segment boundaries, with a fixed number of loads per step (a wave
-// past its last tile re-reads block 0), so every wait before a tile's first
-// use leaves the younger tiles in flight.
+// (the 4 waves of a half take a segment's sub-tiles round-robin) NBUF - 1
+// tiles ahead across segment boundaries, with a fixed number of loads per
+// step (a wave past its last tile re-reads block 0), so every wait before a
+// tile's first use leaves the younger tiles in flight.
 //
 // Merge.  At a segment end a wave deposits its (max, sum, acc) in an LDS merge
-// area and streams on; at its next segment end (or after the batch's closing
-// barrier) it merges a quarter of that segment's output from the 4 deposits,
-// in wave order, and writes it: the output row (unsplit) or the partition's
-// output and natural-log LSE (split).  Counters in LDS order deposits and
-// merges, so no wave waits at a segment end unless another wave is a whole
-// segment behind.  A segment longer than the staged table is carried into the
-// next batch with its running state.
+// area of its half and streams on; at its next segment end (or after the
+// batch's closing barrier) it merges a quarter of that segment's output from
+// the half's 4 deposits, in wave order, and writes it: the output row
+// (unsplit) or the partition's output and natural-log LSE (split).  Counters
+// in LDS order deposits and merges, so no wave waits at a segment end unless
+// another wave of its half is a whole segment behind.  A segment longer than
+// the staged table is carried into the next batch with its running state, by
+// the same half.
 //
 // Tile policy interface (T): constants KV, D, BS, G, E (KV element bytes), EQ
 // (query element bytes), OUT_F32, NBUF, QROWB (staged query row bytes), QBYTES
-// (LDS for staged queries), NPAR (merge areas); types Buf (one sub-tile in
+// (LDS for staged queries), NPAR (merge areas), HALVES (1 or 2); types Buf (one sub-tile in
 // registers, with fields slot and st) and WaveLds (per-wave LDS scratch); and
 // the device members reset(), load(Buf&, k_tile, v_tile, sub),
 // set_query(staged rows), compute(Buf&, t0, t1, qk_scale, WaveLds&) and
