@@ -2,9 +2,13 @@
 """Benchmark of the paged decode-attention step on one MI355X.
 
 A step is one pass of the whole path over one batch: append each sequence's
-new token with pa_reshape_and_cache, attend with pa_decode_split (or
-pa_decode with --mode unsplit) and merge partitions with pa_reduce_lse.
-Inputs are seeded synthetic data already resident in HBM when timing starts.
+new token with pa_reshape_and_cache, then attend in the workload's own mode:
+one pass per (sequence, KV head) with pa_decode, or, for the long-context
+workload whose definition names split-sequence partitions, pa_decode_split
+followed by the pa_reduce_lse merge (--mode overrides).  The default workload
+is the largest one that fits one GPU: 256 sequences with an E4M3 cache and a
+4096-token window.  Inputs are seeded synthetic data already resident in HBM
+when timing starts.
 
 Prints ONE JSON line.  `value` is KV GB/s of the whole step (in-window K+V
 bytes read per step / wall time per step).  `roofline` is the decode kernel's
@@ -33,7 +37,11 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "paged decode attention: KV GB/s (% of MI355X HBM peak) + µs/call"
 EXTEND_METRIC = "paged extend attention: TFLOP/s (% of MI355X bf16 dense matrix peak)"
-DEFAULT_CFG = 2
+DEFAULT_CFG = 5
+# Decode mode of each workload: only the long-context mixed batch is defined
+# with split-sequence partitions (512 tokens) and an LSE reduce; the others are
+# served by one pass per (sequence, KV head).
+DEFAULT_MODE = {1: "unsplit", 2: "unsplit", 3: "split", 4: "unsplit", 5: "unsplit"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 
@@ -325,7 +333,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=DEFAULT_CFG, help="workload 1..5")
-    ap.add_argument("--mode", choices=["split", "unsplit"], default="split")
+    ap.add_argument("--mode", choices=["split", "unsplit"], default=None,
+                    help="decode mode (default: the workload's own, see DEFAULT_MODE)")
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -375,6 +384,8 @@ def main():
     from paged_kv_cache_267_amd.harness import DeviceWorkload
 
     wl = W.config(args.config)
+    if args.mode is None:
+        args.mode = DEFAULT_MODE[args.config]
     pa.pa_set_decode_kernel(args.kernel)
     kv_code = {"f32": pa.PA_F32, "bf16": pa.PA_BF16, "fp8_e4m3": pa.PA_FP8_E4M3}[wl.kv_dtype]
     kernel = pa.pa_decode_kernel_name(kv_code, wl.num_q_heads, wl.num_kv_heads)

@@ -24,8 +24,10 @@
  *
  * Conventions shared by every entry point
  *   - All buffer pointers are DEVICE pointers owned by the caller.  The
- *     library allocates nothing and is reentrant; its only state is the
- *     process-wide decode kernel choice (pa_set_decode_kernel).
+ *     library allocates nothing.  Its state: the decode kernel-family choice
+ *     of each host thread (pa_set_decode_kernel), and per-device launch facts
+ *     (compute units, kernel occupancy) found at a device's first launch and
+ *     kept.  Calls from several host threads may overlap.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Every call validates its arguments on the host, enqueues its kernels on
  *     `stream` and returns without synchronising.  Validation happens before
@@ -216,7 +218,11 @@ int pa_extend(const void* query, const void* key_cache, const void* value_cache,
  * over the non-empty partitions of each row (found from seq_lens,
  * partition_size and sliding_window; the others are not read).  A row with
  * L = 0 gets zeros.  out: [num_seqs][num_q_heads][head_dim] of out_dtype
- * (F32 or BF16).
+ * (F32 or BF16).  seq_lens must be the lengths pa_decode_split was given and
+ * meet its precondition (L <= max_blocks_per_seq * block_size): the split
+ * kernel clamps a longer length to the table's capacity, this merge does not
+ * know that capacity, so for such a row it would merge partitions the split
+ * never wrote and the row is unspecified (reads stay inside the workspace).
  */
 int pa_reduce_lse(const float* part_out, const float* part_lse, const int32_t* seq_lens,
                   int num_seqs, int num_q_heads, int head_dim, int partition_size,
@@ -251,22 +257,22 @@ int pa_fp8_e4m3_dequantize(const uint8_t* codes, float scale, float* out, long l
                            void* stream);
 
 /*
- * Decode kernel family.  Two kernels compute the same operation: a vector-ALU
- * kernel (dot products on the VALU, one workgroup per (KV head, partition,
- * sequence)) and a matrix-core kernel (both contractions on MFMA, persistent
- * balanced schedule; bf16 and E4M3 caches only).  PA_KERNEL_AUTO picks per
- * call from the KV dtype and the group size G = num_q_heads / num_kv_heads;
- * the other values force a family wherever it applies (f32 caches always run
- * the vector-ALU kernel, groups of 16 always the matrix-core kernel).  The choice is process-wide, for tests and tuning;
- * set it before launching work, it is not ordered against calls in flight on
- * other host threads.
+ * Decode kernel family.  Both families run the same persistent, balanced
+ * schedule over (sequence, KV head, partition) segments and differ in the
+ * per-tile arithmetic: a vector-ALU tile (dot products on the VALU) and a
+ * matrix-core tile (both contractions on MFMA; bf16 and E4M3 caches only).
+ * PA_KERNEL_AUTO picks per call from the KV dtype and the group size
+ * G = num_q_heads / num_kv_heads; the other values force a family wherever it
+ * applies (f32 caches always run the vector-ALU tile, groups of 16 always the
+ * matrix-core tile).  The choice is per host thread (a call uses the setting
+ * of the thread that makes it) and exists for tests and tuning.
  */
 typedef enum { PA_KERNEL_AUTO = 0, PA_KERNEL_VALU = 1, PA_KERNEL_MFMA = 2 } pa_kernel_choice;
 
-/* Sets the process-wide choice; PA_ERR_UNSUPPORTED for a value outside the enum. */
+/* Sets the calling thread's choice; PA_ERR_UNSUPPORTED for a value outside the enum. */
 int pa_set_decode_kernel(int choice);
 
-/* The current process-wide choice. */
+/* The calling thread's current choice. */
 int pa_get_decode_kernel(void);
 
 /* Name of the kernel family ("valu" or "mfma") that pa_decode / pa_decode_split

@@ -12,8 +12,7 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# PA_LIBRARY may name another build of the same library (e.g. a tuning variant)
-LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpa.so")
+LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE",
@@ -305,7 +304,7 @@ class BlockManager:
 
 
 def pa_set_decode_kernel(choice) -> None:
-    """Process-wide decode kernel family: "auto", "valu" or "mfma" (or its code)."""
+    """Decode kernel family of the calling thread: "auto", "valu" or "mfma" (or its code)."""
     code = KERNEL_CHOICES[choice] if isinstance(choice, str) else int(choice)
     _check(lib().pa_set_decode_kernel(code))
 

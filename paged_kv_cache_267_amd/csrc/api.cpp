@@ -47,7 +47,6 @@ int check_decode(const void* query, const void* key_cache, const void* value_cac
       block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || sliding_window < 0)
     return PA_ERR_SHAPE;
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
-  if (num_seqs > 65535) return PA_ERR_SHAPE;  // grid z
   if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
     return PA_ERR_SHAPE;
   if ((long long)max_blocks_per_seq * block_size > (1ll << 30)) return PA_ERR_SHAPE;
@@ -239,7 +238,7 @@ int pa_reduce_lse(const float* part_out, const float* part_lse, const int32_t* s
   if (partition_size <= 0 || max_num_partitions <= 0) return PA_ERR_PARTITION;
   if (!aligned16(part_out) || !aligned16(out)) return PA_ERR_ALIGN;
   if (num_seqs == 0) return PA_OK;
-  if (num_seqs > 65535) return PA_ERR_SHAPE;
+  if ((long long)num_seqs * num_q_heads >= (1ll << 31)) return PA_ERR_SHAPE;  // rows in int
   return hip_status(pa::launch_reduce_lse(part_out, part_lse, seq_lens, num_seqs, num_q_heads,
                                           head_dim, partition_size, max_num_partitions,
                                           sliding_window, out, out_dtype == PA_BF16,
@@ -287,11 +286,9 @@ int pa_probe_gather_read(const void* base, const int32_t* ids, long long num_chu
   if (!base || !ids || !sink) return PA_ERR_NULL;
   if (!aligned16(base)) return PA_ERR_ALIGN;
   if (grid == 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      cus = 256;
-    grid = 8 * cus;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    grid = 8 * pa::device_cu_count(dev);
   }
   return hip_status(pa::launch_gather_read_probe(base, ids, num_chunks, chunk_bytes, sink, grid,
                                                  (hipStream_t)stream));

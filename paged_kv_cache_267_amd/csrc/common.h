@@ -28,6 +28,14 @@ template <> struct KvTraits<KV_F32> { static constexpr int E = 4; };
 template <> struct KvTraits<KV_BF16> { static constexpr int E = 2; };
 template <> struct KvTraits<KV_FP8> { static constexpr int E = 1; };
 
+// Devices whose launch facts (compute units, occupancy) are cached; a device
+// index beyond this is queried on every launch.
+constexpr int PA_MAX_DEVICES = 64;
+
+// Compute units of device dev (host side; 256 if dev < 0 or the query fails),
+// queried once per device and kept.
+int device_cu_count(int dev);
+
 // Parameters of one decode launch (unsplit when part_out == nullptr).
 struct DecodeParams {
   const void* q;
@@ -45,7 +53,6 @@ struct DecodeParams {
   int partition_size;   // tokens per partition (split); 0 = whole sequence
   int max_parts;
   int seq_begin, seq_count;  // sequences of this launch (persistent schedule)
-  int pairs;            // the grid is two workgroups per CU, j and j + J/2 of a head together
 };
 
 // Parameters of one multi-token (extend) launch.  Sequence s owns query rows

@@ -55,6 +55,8 @@
 // deposit(m[G], l[G], acc[G][D + 4]).
 #pragma once
 
+#include <atomic>
+
 #include "common.h"
 
 namespace pa {
@@ -64,9 +66,6 @@ constexpr int PD_SEQ_CHUNK = 1024;    // sequences per launch (schedule kept in 
 constexpr int PD_TBL = 2048;          // block-table entries staged per batch
 constexpr int PD_SORT_MAX = 512;      // partial segments ordered by size (more: by sequence)
 constexpr int PD_SIZE_CLASSES = 64;   // size classes of that order (one per lane of a wave)
-// Share of a CU pair's sub-tiles taken by the pair's older workgroup (see the
-// dealing below).
-constexpr float PD_OLDER_SHARE = 0.6f;
 
 // Per-batch description of one segment slot.
 struct SegMeta {
@@ -280,55 +279,12 @@ __global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_k
   if (tid == 0) sm.carry_half = 0;
   __syncthreads();
   const int total = F + NPART;
-  // The list is dealt in serpentine order: round r gives dealing slot d entry
-  // r*JD + d (r even) or r*JD + JD-1-d (r odd), so the largest entries of one
-  // round meet the smallest of the next.  Dealing slots are the J workgroups,
-  // or, when the grid holds two workgroups per CU (workgroups j and j + J/2
-  // of a head share a CU), the J/2 CU pairs: the older workgroup of a pair
-  // (dispatched first, j < J/2) is served faster by the CU, so it takes the
-  // prefix of the pair's entries that holds PD_OLDER_SHARE of their sub-tiles
-  // and the younger one the rest.
-  const bool pairs = p.pairs != 0 && sorted && (J % 2) == 0;
-  const int JD = pairs ? J / 2 : J, jd = pairs ? j % (J / 2) : j;
-  auto deal = [&](int m) -> int { return m * JD + ((m & 1) ? JD - 1 - jd : jd); };
-  int MD = total / JD;  // full rounds, then possibly one entry of the last round
-  if (MD * JD < total && deal(MD) < total) ++MD;
-  int M = MD, m_lo = 0;
-  if (pairs) {
-    auto entry_tiles = [&](int k) -> int {  // sub-tiles of list entry k (at least 1)
-      if (k < F) return P >> 4;
-      const int e = sm.plist[k - F];
-      int t0, t1;
-      seg_range(sm.lens[e >> 20], e & 0xfffff, t0, t1);
-      return t0 < t1 ? max(1, ((t1 + 15) >> 4) - (t0 >> 4)) : 1;
-    };
-    int W = 0;
-    for (int m0 = 0; m0 < MD; m0 += 64) {
-      int x = m0 + lane < MD ? entry_tiles(deal(m0 + lane)) : 0;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-      W += x;
-    }
-    // the older workgroup takes entries whose midpoint lies below the target
-    const int target2 = (int)(2.0f * PD_OLDER_SHARE * (float)W);
-    int split = MD, run = 0;
-    for (int m0 = 0; m0 < MD && split == MD; m0 += 64) {
-      const int sz = m0 + lane < MD ? entry_tiles(deal(m0 + lane)) : 0;
-      int incl = sz;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += y;
-      }
-      const int excl = run + incl - sz;
-      const uint64_t past = __builtin_amdgcn_ballot_w64(m0 + lane < MD && 2 * excl + sz >= target2);
-      if (past) split = m0 + (int)__builtin_ctzll(past);
-      run += __shfl(incl, 63, 64);
-    }
-    split = uniform(split);
-    if (j < J / 2) { M = split; } else { m_lo = split; M = MD - split; }
-  }
-  auto list_index = [&](int m) -> int { return deal(m_lo + m); };
+  // The list is dealt to the head's J workgroups in serpentine order: round r
+  // gives workgroup j entry r*J + j (r even) or r*J + J-1-j (r odd), so the
+  // largest entries of one round meet the smallest of the next.
+  auto list_index = [&](int m) -> int { return m * J + ((m & 1) ? J - 1 - j : j); };
+  int M = total / J;  // full rounds, then possibly one entry of the last round
+  if (M * J < total && list_index(M) < total) ++M;
 
   // k-th segment of the list -> (sequence, partition), in each lane on its
   // own: a sorted partial segment is read from the ordered list; otherwise a
@@ -465,7 +421,9 @@ __global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_k
         if (pl >= off) incl += y;
       }
       const uint64_t stop = __builtin_amdgcn_ballot_w64(!have || incl > PD_TBL);
-      const int f = (int)__builtin_ctzll(stop);     // lanes >= SLOTS never have a slot
+      // first lane that takes no slot; 64 when every lane takes one (SLOTS = 64
+      // and the batch's blocks all fit), where the ballot is empty
+      const int f = stop != 0 ? (int)__builtin_ctzll(stop) : 64;
       const bool trunc = f == 0;                    // the first slot alone overflows the table
       const int cnt = trunc ? 1 : f;
       int b = st_hi;
@@ -682,22 +640,22 @@ __global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_k
 }
 
 // Grid: resident capacity, a multiple of num_kv_heads; sequences in launches
-// of PD_SEQ_CHUNK.
+// of PD_SEQ_CHUNK.  The resident workgroups per CU of this kernel are found
+// once per device (the first launch there) and kept.
 template <class T>
 hipError_t launch_decode_persistent(const DecodeParams& p0, hipStream_t stream) {
-  static int per_cu = -1;
-  if (per_cu < 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_persistent_kernel<T>,
+  static std::atomic<int> per_cu_of[PA_MAX_DEVICES];   // 0: not yet known
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= PA_MAX_DEVICES) dev = -1;
+  int per_cu = dev >= 0 ? per_cu_of[dev].load(std::memory_order_relaxed) : 0;
+  if (per_cu <= 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_persistent_kernel<T>,
                                                      64 * PD_WAVES * T::HALVES, 0) != hipSuccess ||
-        n < 1)
-      n = 1;
-    per_cu = n;
+        per_cu < 1)
+      per_cu = 1;
+    if (dev >= 0) per_cu_of[dev].store(per_cu, std::memory_order_relaxed);
   }
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus = 256;
+  const int cus = device_cu_count(dev);
   const int H = p0.num_kv_heads;
   DecodeParams p = p0;
   for (int s0 = 0; s0 < p0.num_seqs; s0 += PD_SEQ_CHUNK) {
@@ -707,8 +665,6 @@ hipError_t launch_decode_persistent(const DecodeParams& p0, hipStream_t stream) 
     long long J = ((long long)cus * per_cu + H - 1) / H;
     if (J > work) J = work;
     if (J < 1) J = 1;
-    // the first J*H/2 workgroups are dispatched one per CU, the rest pair up with them
-    p.pairs = (per_cu == 2 && J * H == 2LL * cus) ? 1 : 0;
     hipLaunchKernelGGL((decode_persistent_kernel<T>), dim3((unsigned)(J * H)),
                        dim3(64 * PD_WAVES * T::HALVES), 0, stream, p);
     const hipError_t e = hipGetLastError();

@@ -7,14 +7,30 @@
 
 namespace pa {
 
-static std::atomic<int> g_choice{PA_KERNEL_AUTO};
+// The kernel-family choice belongs to the calling host thread: a call reads
+// the setting of the thread that makes it, so threads never race on it.
+static thread_local int g_choice = PA_KERNEL_AUTO;
+
+int device_cu_count(int dev) {
+  static std::atomic<int> cached[PA_MAX_DEVICES];   // 0: not yet known
+  if (dev >= 0 && dev < PA_MAX_DEVICES) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    return 256;
+  if (dev < PA_MAX_DEVICES) cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 
 int set_decode_kernel(int choice) {
   if (choice != PA_KERNEL_AUTO && choice != PA_KERNEL_VALU && choice != PA_KERNEL_MFMA) return -1;
-  g_choice.store(choice, std::memory_order_relaxed);
+  g_choice = choice;
   return 0;
 }
-int get_decode_kernel() { return g_choice.load(std::memory_order_relaxed); }
+int get_decode_kernel() { return g_choice; }
 
 // Automatic choice: the matrix cores take groups of 8 or more query heads per
 // KV head; smaller groups use the VALU bandwidth path (f32 caches always do).

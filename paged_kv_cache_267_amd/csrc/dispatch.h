@@ -18,8 +18,8 @@ hipError_t decode_valu_fp8(const DecodeParams& p, int D, int BS, int G, hipStrea
 hipError_t decode_mfma_bf16(const DecodeParams& p, int D, int BS, int G, hipStream_t stream);
 hipError_t decode_mfma_fp8(const DecodeParams& p, int D, int BS, int G, hipStream_t stream);
 
-// Process-wide kernel-family choice (pa_kernel_choice); set returns -1 for an
-// unknown value.
+// Kernel-family choice (pa_kernel_choice) of the calling host thread; set
+// returns -1 for an unknown value.
 int set_decode_kernel(int choice);
 int get_decode_kernel();
 

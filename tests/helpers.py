@@ -59,6 +59,13 @@ def widen(raw: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
+def half_ulp_bf16(x):
+    """Half the spacing of bf16 numbers at |x| (8 significand bits): the
+    error of the correctly rounded bf16 output itself."""
+    a = np.maximum(np.abs(x), 2.0 ** -126)
+    return 0.5 * np.exp2(np.floor(np.log2(a)) - 7)
+
+
 def err_stats(got: np.ndarray, ref: np.ndarray):
     d = np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))
     return float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0

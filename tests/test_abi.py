@@ -58,7 +58,8 @@ def split(**kw):
     (dict(qdt=0, kvdt=1), 2), (dict(qdt=1, kvdt=0), 2), (dict(qdt=2, kvdt=2), 2),
     (dict(kvdt=9), 2),
     (dict(S=-1), 3), (dict(Hq=0), 3), (dict(Hq=6, Hkv=4), 3), (dict(mb=0), 3), (dict(nb=0), 3),
-    (dict(win=-1), 3), (dict(scale=float("nan")), 3), (dict(S=70000), 3),
+    (dict(win=-1), 3), (dict(scale=float("nan")), 3),
+    (dict(S=1 << 29, mb=4), 3),   # block-table index beyond int32
     (dict(D=96), 4), (dict(bs=8), 4), (dict(bs=128), 4), (dict(Hq=6, Hkv=2), 4),
     (dict(Hq=64, Hkv=2), 4),
     (dict(out=ODD), 7), (dict(q=ODD), 7),
@@ -142,6 +143,7 @@ def test_reduce_validation():
     assert call(6, 0) == 5
     assert call(9, ODD) == 7
     assert call(3, 0) == 0
+    assert call(3, 1 << 28) == 3   # rows (sequence x head) beyond int32
 
 
 def test_workspace_bytes():
@@ -176,6 +178,20 @@ def test_decode_kernel_choice():
     assert pa.pa_decode_kernel_name(7, 8, 8) == ""
     assert L.pa_set_decode_kernel(3) == 4 and L.pa_set_decode_kernel(-1) == 4
     assert pa.pa_get_decode_kernel() == "auto"
+
+
+def test_decode_kernel_choice_is_per_thread():
+    """A choice set on one host thread does not change another thread's calls."""
+    import threading
+    seen = {}
+    with pa.decode_kernel("valu"):
+        t = threading.Thread(target=lambda: seen.update(
+            other=pa.pa_get_decode_kernel(),
+            name=pa.pa_decode_kernel_name(pa.PA_BF16, 64, 8)))
+        t.start()
+        t.join()
+        assert pa.pa_get_decode_kernel() == "valu"
+    assert seen == {"other": "auto", "name": "mfma"}
 
 
 def test_probe_validation():
