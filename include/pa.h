@@ -91,7 +91,8 @@ typedef enum {
   PA_ERR_PARTITION = 5,   /* bad partition_size / max_num_partitions           */
   PA_ERR_HIP = 6,         /* a kernel launch failed                            */
   PA_ERR_ALIGN = 7,       /* a buffer is not 16-byte aligned                   */
-  PA_ERR_EXHAUSTED = 8    /* the block pool has too few free blocks            */
+  PA_ERR_EXHAUSTED = 8,   /* the block pool has too few free blocks            */
+  PA_ERR_SCRATCH = 9      /* workspace beyond PA_NOALLOC_SCRATCH_BYTES         */
 } pa_status;
 
 /*
@@ -241,6 +242,30 @@ int pa_reduce_lse(const float* part_out, const float* part_lse, const int32_t* s
  * -PA_ERR_SHAPE (n < 0, or max_waste_frac not in (0, 1]).
  */
 int pa_choose_block_size(const int32_t* seq_lens, int n, double max_waste_frac);
+
+/*
+ * pa_decode_split_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): pa_decode_split followed by pa_reduce_lse in one call, with
+ * the partition workspace in a device array the library holds, so the call
+ * allocates nothing.  Arguments are pa_decode's, then partition_size;
+ * out [num_seqs][num_q_heads][head_dim] is of q_dtype.  The number of
+ * partitions is ceil(max_blocks_per_seq * block_size / partition_size), and
+ * the workspace, pa_decode_split_workspace_bytes(num_seqs, num_q_heads,
+ * head_dim, that number), must fit in PA_NOALLOC_SCRATCH_BYTES
+ * (PA_ERR_SCRATCH otherwise, before any HIP call).  Every GPU the library
+ * runs on holds one such array from its first use until the process ends.
+ * Calls that overlap on one GPU (other streams or host threads) share it and
+ * race: order them.  Results equal pa_decode_split + pa_reduce_lse on the
+ * same arguments.  Other errors as pa_decode_split.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int pa_decode_split_noalloc(const void* query, const void* key_cache, const void* value_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens, int block_size,
+                            float scale, void* out, int num_seqs, int num_q_heads,
+                            int num_kv_heads, int head_dim, int max_blocks_per_seq,
+                            int num_blocks, int sliding_window, int q_dtype, int kv_dtype,
+                            float k_scale, float v_scale, int partition_size, void* stream);
 
 /* Bytes of part_out + part_lse for pa_decode_split (part_lse starts at
    offset num_seqs*num_q_heads*max_num_partitions*head_dim*4). */

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE",
           4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_PARTITION", 6: "PA_ERR_HIP", 7: "PA_ERR_ALIGN",
-          8: "PA_ERR_EXHAUSTED"}
+          8: "PA_ERR_EXHAUSTED", 9: "PA_ERR_SCRATCH"}
 
 # exported symbols (include/pa.h)
 EXPORTS = ("pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_reduce_lse",
@@ -27,7 +27,8 @@ EXPORTS = ("pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_reduce_ls
            "pa_choose_block_size", "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free",
            "pa_bm_new_sequence", "pa_bm_append", "pa_bm_release_before", "pa_bm_free_sequence",
            "pa_bm_reclaim", "pa_bm_block_table", "pa_bm_seq_len", "pa_bm_refcount",
-           "pa_extend")
+           "pa_extend", "pa_decode_split_noalloc")
+NOALLOC_SCRATCH_BYTES = 128 << 20   # PA_NOALLOC_SCRATCH_BYTES
 KERNEL_CHOICES = {"auto": 0, "valu": 1, "mfma": 2}
 
 
@@ -62,6 +63,8 @@ def lib() -> ctypes.CDLL:
     L.pa_decode.argtypes = [P, P, P, P, P, I, F, P, I, I, I, I, I, I, I, I, I, F, F, P]
     L.pa_decode_split.argtypes = [P, P, P, P, P, I, F, I, I, I, I, I, I, I, I, I, F, F, I, I, P,
                                   P, P]
+    L.pa_decode_split_noalloc.argtypes = [P, P, P, P, P, I, F, P, I, I, I, I, I, I, I, I, I, F, F,
+                                          I, P]
     L.pa_reduce_lse.argtypes = [P, P, P, I, I, I, I, I, I, P, I, P]
     L.pa_extend.argtypes = [P, P, P, P, P, P, I, F, P, I, I, I, I, I, I, I, I, I, I, I, F, F, P]
     L.pa_decode_split_workspace_bytes.argtypes = [I, I, I, I]
@@ -91,7 +94,7 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_kernel_name.argtypes = [I, I, I]
     L.pa_decode_kernel_name.restype = ctypes.c_char_p
     for name in ("pa_choose_block_size", "pa_reshape_and_cache_fp8", "pa_probe_gather_read", "pa_set_decode_kernel", "pa_get_decode_kernel", "pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_reduce_lse",
-                 "pa_fp8_e4m3_dequantize", "pa_extend"):
+                 "pa_fp8_e4m3_dequantize", "pa_extend", "pa_decode_split_noalloc"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -180,6 +183,20 @@ def pa_decode_split(query, key_cache, value_cache, block_tables, seq_lens, *, bl
         _dtype_code(query), _dtype_code(key_cache), float(k_scale), float(v_scale),
         int(partition_size), int(max_num_partitions), _ptr(part_out), _ptr(part_lse),
         _stream(stream)))
+
+
+def pa_decode_split_noalloc(query, key_cache, value_cache, block_tables, seq_lens, *,
+                            block_size, scale, out, num_kv_heads, partition_size,
+                            sliding_window=0, k_scale=1.0, v_scale=1.0, stream=None) -> None:
+    """Split decode + LSE merge into ``out`` [S, Hq, D] (query dtype) with the
+    partition workspace in the library's own device array (no allocation)."""
+    S, Hq, D = query.shape
+    _check(lib().pa_decode_split_noalloc(
+        _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables), _ptr(seq_lens),
+        block_size, float(scale), _ptr(out), S, Hq, num_kv_heads, D, block_tables.shape[1],
+        _num_blocks(key_cache, num_kv_heads, D, block_size), int(sliding_window),
+        _dtype_code(query), _dtype_code(key_cache), float(k_scale), float(v_scale),
+        int(partition_size), _stream(stream)))
 
 
 def pa_extend(query, key_cache, value_cache, block_tables, seq_lens, query_start_loc, *,

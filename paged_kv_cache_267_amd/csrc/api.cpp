@@ -12,8 +12,10 @@
 #include "dispatch.h"
 
 namespace {
-
 thread_local std::string g_hip_error;
+}  // namespace
+
+namespace pa {
 
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return PA_OK;
@@ -35,7 +37,6 @@ bool group_supported(int kv_dtype, int G) {
   return G == 16 && kv_dtype != PA_F32;
 }
 
-// Checks shared by pa_decode and pa_decode_split.
 int check_decode(const void* query, const void* key_cache, const void* value_cache,
                  const int32_t* block_tables, const int32_t* seq_lens, int block_size,
                  float scale, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
@@ -59,12 +60,12 @@ int check_decode(const void* query, const void* key_cache, const void* value_cac
   return PA_OK;
 }
 
-pa::DecodeParams make_params(const void* query, const void* key_cache, const void* value_cache,
+DecodeParams make_params(const void* query, const void* key_cache, const void* value_cache,
                              const int32_t* block_tables, const int32_t* seq_lens, float scale,
                              int num_seqs, int num_q_heads, int num_kv_heads,
                              int max_blocks_per_seq, int num_blocks, int sliding_window,
                              float k_scale, float v_scale) {
-  pa::DecodeParams p{};
+  DecodeParams p{};
   p.q = query;
   p.kc = key_cache;
   p.vc = value_cache;
@@ -81,7 +82,25 @@ pa::DecodeParams make_params(const void* query, const void* key_cache, const voi
   return p;
 }
 
-}  // namespace
+int check_partition(int block_size, int max_blocks_per_seq, int partition_size,
+                    int max_num_partitions) {
+  if (partition_size <= 0 || partition_size % block_size != 0 || max_num_partitions <= 0 ||
+      max_num_partitions > 65535)
+    return PA_ERR_PARTITION;
+  if ((long long)max_num_partitions * partition_size < (long long)max_blocks_per_seq * block_size)
+    return PA_ERR_PARTITION;
+  return PA_OK;
+}
+
+}  // namespace pa
+
+using pa::aligned16;
+using pa::check_decode;
+using pa::check_partition;
+using pa::elem_bytes;
+using pa::group_supported;
+using pa::hip_status;
+using pa::make_params;
 
 extern "C" {
 
@@ -159,11 +178,8 @@ int pa_decode_split(const void* query, const void* key_cache, const void* value_
                         num_blocks, sliding_window, q_dtype, kv_dtype, k_scale, v_scale);
   if (st != PA_OK) return st;
   if (!part_out || !part_lse) return PA_ERR_NULL;
-  if (partition_size <= 0 || partition_size % block_size != 0 || max_num_partitions <= 0 ||
-      max_num_partitions > 65535)
-    return PA_ERR_PARTITION;
-  if ((long long)max_num_partitions * partition_size < (long long)max_blocks_per_seq * block_size)
-    return PA_ERR_PARTITION;
+  st = check_partition(block_size, max_blocks_per_seq, partition_size, max_num_partitions);
+  if (st != PA_OK) return st;
   if (!aligned16(part_out)) return PA_ERR_ALIGN;
   if (num_seqs == 0) return PA_OK;
   pa::DecodeParams p = make_params(query, key_cache, value_cache, block_tables, seq_lens, scale,
@@ -319,6 +335,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_HIP: return "HIP kernel launch failed";
     case PA_ERR_ALIGN: return "a buffer is not 16-byte aligned";
     case PA_ERR_EXHAUSTED: return "the block pool has too few free blocks";
+    case PA_ERR_SCRATCH: return "the partition workspace exceeds the library's fixed scratch array";
     default: return "unknown status";
   }
 }

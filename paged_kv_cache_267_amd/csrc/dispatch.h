@@ -27,6 +27,22 @@ int get_decode_kernel();
 // current choice.
 bool decode_uses_mfma(int kv_dtype, int G);
 
+// Host-side argument handling shared by the entry points of api.cpp and
+// noalloc.cpp: checks return a pa_status (PA_OK when the call may proceed).
+int hip_status(hipError_t e);   // PA_OK, or PA_ERR_HIP with the text kept per thread
+bool aligned16(const void* p);
+int check_decode(const void* query, const void* key_cache, const void* value_cache,
+                 const int32_t* block_tables, const int32_t* seq_lens, int block_size,
+                 float scale, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                 int max_blocks_per_seq, int num_blocks, int sliding_window, int q_dtype,
+                 int kv_dtype, float k_scale, float v_scale);
+int check_partition(int block_size, int max_blocks_per_seq, int partition_size,
+                    int max_num_partitions);
+DecodeParams make_params(const void* query, const void* key_cache, const void* value_cache,
+                         const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                         int num_seqs, int num_q_heads, int num_kv_heads, int max_blocks_per_seq,
+                         int num_blocks, int sliding_window, float k_scale, float v_scale);
+
 // Chooses the tile computation for (KV dtype, group size) and launches it.
 hipError_t dispatch_decode(const DecodeParams& p, int kv_dtype, int D, int BS, int G,
                            hipStream_t stream);

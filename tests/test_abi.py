@@ -146,13 +146,42 @@ def test_reduce_validation():
     assert call(3, 1 << 28) == 3   # rows (sequence x head) beyond int32
 
 
+def noalloc(**kw):
+    args = dict(q=A, kc=A, vc=A, bt=A, sl=A, bs=16, scale=0.125, out=B, S=2, Hq=8, Hkv=2, D=128,
+                mb=4, nb=8, win=0, qdt=1, kvdt=1, ks=1.0, vs=1.0, P=32, stream=NULL)
+    args.update(kw)
+    return pa.lib().pa_decode_split_noalloc(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), 1), (dict(out=NULL), 1), (dict(qdt=0), 2), (dict(D=96), 4),
+    (dict(out=ODD), 7), (dict(P=0), 5), (dict(P=24), 5), (dict(P=-16), 5),
+    (dict(mb=1 << 20, bs=16, P=16, S=1), 5),             # more than 65535 partitions
+    # workspace of 4096 x 64 heads x 2048 partitions: beyond the fixed array
+    (dict(S=4096, Hq=64, Hkv=8, mb=2048, P=16), 9),
+    # 8 x 8 heads x 128 partitions x 129 floats: 4.2 MB, fits; S = 0 is a no-op
+    (dict(S=0, mb=1024, P=128), 0),
+])
+def test_noalloc_validation(kw, status):
+    """Every rejection, the size limit included, happens before any HIP call."""
+    assert noalloc(**kw) == status
+
+
+def test_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    assert "#define PA_NOALLOC_SCRATCH_BYTES (128u << 20)" in text
+    assert pa.NOALLOC_SCRATCH_BYTES == 128 << 20
+    # the long-context split workload (16 x 64 heads x 128 partitions of D 128) fits
+    assert pa.pa_decode_split_workspace_bytes(16, 64, 128, 128) <= pa.NOALLOC_SCRATCH_BYTES
+
+
 def test_workspace_bytes():
     assert pa.pa_decode_split_workspace_bytes(3, 8, 128, 5) == 3 * 8 * 5 * (128 + 1) * 4
     assert pa.pa_decode_split_workspace_bytes(0, 8, 128, 5) == 0
 
 
 def test_status_strings():
-    for s in range(9):
+    for s in range(10):
         assert pa.lib().pa_status_string(s)
 
 
