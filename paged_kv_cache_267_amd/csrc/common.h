@@ -185,6 +185,14 @@ __device__ __forceinline__ int lds_exchange_acq_rel(int32_t* p, int v) {
   return r;
 }
 
+// Orders the calling wave's LDS writes before its following LDS reads, so
+// its lanes read what other lanes of the same wave wrote.
+__device__ __forceinline__ void lds_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 // Workgroup barrier ordering LDS only: the calling waves' outstanding global
 // loads stay in flight across it (a full __syncthreads would drain them).
 __device__ __forceinline__ void lds_barrier() {

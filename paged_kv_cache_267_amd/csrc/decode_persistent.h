@@ -65,7 +65,7 @@ constexpr int PD_WAVES = 4;
 constexpr int PD_SEQ_CHUNK = 1024;    // sequences per launch (schedule kept in LDS)
 constexpr int PD_TBL = 2048;          // block-table entries staged per batch
 constexpr int PD_SORT_MAX = 512;      // partial segments ordered by size (more: by sequence)
-constexpr int PD_SIZE_CLASSES = 64;   // size classes of that order (one per lane of a wave)
+constexpr int PD_SIZE_CLASSES = 256;  // size classes of that order (16 per octave of sub-tiles)
 
 // Per-batch description of one segment slot.
 struct SegMeta {
@@ -195,15 +195,17 @@ __global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_k
   const int F = uniform(sm.fpre[S]), NPART = uniform(sm.ppre[S]);
   const bool sorted = NPART <= PD_SORT_MAX;
   if (sorted) {
-    // list the partial segments with a size class (4 classes per octave;
-    // larger segments get smaller classes), then order them by class with a
-    // stable counting sort, so every workgroup derives the same order
-    constexpr int NBK = PD_SIZE_CLASSES, CHUNKS = PD_SORT_MAX / 64, SR = PD_SORT_MAX / NTH;
-    static_assert(NBK == 64, "one size class per lane");
+    // list the partial segments with a size class, then order them by class
+    // with a stable counting sort, so every workgroup derives the same order
+    constexpr int NBK = PD_SIZE_CLASSES, SR = PD_SORT_MAX / NTH;
+    constexpr int CBITS = 8, CPL = NBK / 64;   // class bits; classes per lane in the scan
+    static_assert(NBK == 1 << CBITS && NBK % 64 == 0, "size classes");
+    // class of a segment of sz sub-tiles: 16 classes per octave (sizes within
+    // 1/16 of each other share one), larger segments in smaller classes
     auto size_class = [](int sz) -> int {
       if (sz <= 0) return NBK - 1;
       const int lz = 31 - __builtin_clz(sz);
-      const int c = lz >= 2 ? 4 * lz + ((sz >> (lz - 2)) & 3) : sz;
+      const int c = lz >= 4 ? 16 * lz + ((sz >> (lz - 4)) & 15) : sz;
       return NBK - 1 - min(NBK - 1, c);
     };
     for (int i = tid; i < S; i += NTH) {
@@ -219,16 +221,17 @@ __global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_k
           seg_range(L, pp, t0, t1);
           if (P != 0 && t1 - t0 == P) continue;
           sm.plist[o] = (i << 20) | pp;
-          sm.u.srt.cls[o] = size_class(t1 - t0);
+          sm.u.srt.cls[o] = size_class(t0 < t1 ? ((t1 + 15) >> 4) - (t0 >> 4) : 0);
           ++o;
         }
       }
     }
-    for (int i = tid; i < CHUNKS * NBK; i += NTH) (&sm.u.srt.cnt[0][0])[i] = 0;
+    const int nch = (NPART + 63) / 64;   // chunks holding entries
+    for (int i = tid; i < nch * NBK; i += NTH) (&sm.u.srt.cnt[0][0])[i] = 0;
     __syncthreads();
     // entry e sits in chunk e / 64 (one wave's lanes); the lanes holding its
-    // class are found bit-sliced (one ballot per bit of the 6-bit class), so
-    // its rank among the chunk's entries of that class costs a fixed 7 ballots
+    // class are found bit-sliced (one ballot per bit of the 8-bit class), so
+    // its rank among the chunk's entries of that class costs a fixed 9 ballots
     int mine[SR], cls[SR], wr[SR];
 #pragma unroll
     for (int r = 0; r < SR; ++r) {
@@ -238,7 +241,7 @@ __global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_k
       cls[r] = valid ? sm.u.srt.cls[e] : 0;
       uint64_t same = __builtin_amdgcn_ballot_w64(valid);
 #pragma unroll
-      for (int bit = 0; bit < 6; ++bit) {
+      for (int bit = 0; bit < CBITS; ++bit) {
         const bool set = (cls[r] >> bit) & 1;
         const uint64_t bm = __builtin_amdgcn_ballot_w64(valid && set);
         same &= set ? bm : ~bm;
@@ -247,11 +250,13 @@ __global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_k
       if (valid && wr[r] == 0) sm.u.srt.cnt[c][cls[r]] = __builtin_popcountll(same);
     }
     __syncthreads();
-    // class starts (exclusive scan over classes of the chunk totals), then each
-    // chunk's base within its class, written over the counts
+    // class starts (exclusive scan over classes of the chunk totals; lane l
+    // holds classes CPL*l ..), then each chunk's base within its class,
+    // written over the counts
     if (wave == 0) {
       int tot = 0;
-      for (int c = 0; c < CHUNKS; ++c) tot += sm.u.srt.cnt[c][lane];
+      for (int k = 0; k < CPL; ++k)
+        for (int c = 0; c < nch; ++c) tot += sm.u.srt.cnt[c][CPL * lane + k];
       int x = tot;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -259,11 +264,12 @@ __global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_k
         if (lane >= off) x += y;
       }
       int run = x - tot;
-      for (int c = 0; c < CHUNKS; ++c) {
-        const int n = sm.u.srt.cnt[c][lane];
-        sm.u.srt.cnt[c][lane] = run;
-        run += n;
-      }
+      for (int k = 0; k < CPL; ++k)
+        for (int c = 0; c < nch; ++c) {
+          const int n = sm.u.srt.cnt[c][CPL * lane + k];
+          sm.u.srt.cnt[c][CPL * lane + k] = run;
+          run += n;
+        }
     }
     __syncthreads();
 #pragma unroll
@@ -321,7 +327,6 @@ __global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_k
       pp = (r == 0 && first_partial) ? p_lo : p_hi - 1;
     }
   };
-
   const char* kbase = (const char*)p.kc + (size_t)hk * TILE_BYTES;
   const char* vbase = (const char*)p.vc + (size_t)hk * TILE_BYTES;
   const size_t block_stride = (size_t)H * TILE_BYTES;

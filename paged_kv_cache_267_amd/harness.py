@@ -52,12 +52,16 @@ class DeviceWorkload:
         self.new_key = _upload(wl.new_key, wl.kv_dtype, d)
         self.new_value = _upload(wl.new_value, wl.kv_dtype, d)
         self.new_slots = torch.from_numpy(wl.new_slots).to(d)
-        self.out = torch.empty_like(self.query)
+        # outputs and partition workspace start as NaN: a row or partition the
+        # kernels fail to write shows up in every comparison
+        self.out = torch.full_like(self.query, float("nan"))
         P = wl.max_blocks_per_seq * wl.block_size
         self.max_parts = max(1, -(-P // self.partition_size))
         S, Hq, D = wl.num_seqs, wl.num_q_heads, wl.head_dim
-        self.part_out = torch.empty((S, Hq, self.max_parts, D), dtype=torch.float32, device=d)
-        self.part_lse = torch.empty((S, Hq, self.max_parts), dtype=torch.float32, device=d)
+        self.part_out = torch.full((S, Hq, self.max_parts, D), float("nan"), dtype=torch.float32,
+                                   device=d)
+        self.part_lse = torch.full((S, Hq, self.max_parts), float("nan"), dtype=torch.float32,
+                                   device=d)
         self.query_start_loc = (torch.from_numpy(wl.query_start_loc).to(d)
                                 if wl.query_start_loc is not None else None)
 
