@@ -1,15 +1,15 @@
 // api.cpp -- the C ABI of libpa.so (include/pa.h): host-side validation and
 // dispatch to the gfx950 kernel instances.  Validation finishes before the
 // first HIP call, so invalid calls never touch the device.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <cmath>
 #include <cstdint>
 #include <string>
 
 #include "../../include/pa.h"
-#include "common.h"
 #include "dispatch.h"
+#include "params.h"
 
 namespace {
 thread_local std::string g_hip_error;
@@ -191,6 +191,40 @@ int pa_decode_split(const void* query, const void* key_cache, const void* value_
   p.max_parts = max_num_partitions;
   return hip_status(pa::dispatch_decode(p, kv_dtype, head_dim, block_size,
                                         num_q_heads / num_kv_heads, (hipStream_t)stream));
+}
+
+int pa_decode_split_noalloc(const void* query, const void* key_cache, const void* value_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens, int block_size,
+                            float scale, void* out, int num_seqs, int num_q_heads,
+                            int num_kv_heads, int head_dim, int max_blocks_per_seq,
+                            int num_blocks, int sliding_window, int q_dtype, int kv_dtype,
+                            float k_scale, float v_scale, int partition_size, void* stream) {
+  // every check, the workspace size included, happens before any HIP call
+  int st = check_decode(query, key_cache, value_cache, block_tables, seq_lens, block_size, scale,
+                        num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                        num_blocks, sliding_window, q_dtype, kv_dtype, k_scale, v_scale);
+  if (st != PA_OK) return st;
+  if (!out) return PA_ERR_NULL;
+  if (!aligned16(out)) return PA_ERR_ALIGN;
+  if (partition_size <= 0) return PA_ERR_PARTITION;
+  const long long span = (long long)max_blocks_per_seq * block_size;
+  const long long parts = (span + partition_size - 1) / partition_size;
+  if (parts > 65535) return PA_ERR_PARTITION;
+  st = check_partition(block_size, max_blocks_per_seq, partition_size, (int)parts);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return PA_OK;
+  if (pa_decode_split_workspace_bytes(num_seqs, num_q_heads, head_dim, (int)parts) >
+      PA_NOALLOC_SCRATCH_BYTES)
+    return PA_ERR_SCRATCH;
+  pa::DecodeParams p = make_params(query, key_cache, value_cache, block_tables, seq_lens, scale,
+                                   num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq,
+                                   num_blocks, sliding_window, k_scale, v_scale);
+  p.out = out;
+  p.partition_size = partition_size;
+  p.max_parts = (int)parts;
+  return hip_status(pa::decode_split_noalloc(p, kv_dtype, head_dim, block_size,
+                                             num_q_heads / num_kv_heads, q_dtype == PA_BF16,
+                                             (hipStream_t)stream));
 }
 
 int pa_extend(const void* query, const void* key_cache, const void* value_cache,

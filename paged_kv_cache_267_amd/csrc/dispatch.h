@@ -1,9 +1,9 @@
 // dispatch.h -- host-side entry points of the kernel instances.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
-#include "common.h"
+#include "params.h"
 
 namespace pa {
 
@@ -42,6 +42,12 @@ DecodeParams make_params(const void* query, const void* key_cache, const void* v
                          const int32_t* block_tables, const int32_t* seq_lens, float scale,
                          int num_seqs, int num_q_heads, int num_kv_heads, int max_blocks_per_seq,
                          int num_blocks, int sliding_window, float k_scale, float v_scale);
+
+// Split decode + LSE merge with the partition workspace (part_out, then
+// part_lse, for p.max_parts partitions) in the library's own device array
+// (noalloc.cpp); p is a split launch whose arguments have been checked.
+hipError_t decode_split_noalloc(DecodeParams p, int kv_dtype, int D, int BS, int G, bool out_bf16,
+                                hipStream_t stream);
 
 // Chooses the tile computation for (KV dtype, group size) and launches it.
 hipError_t dispatch_decode(const DecodeParams& p, int kv_dtype, int D, int BS, int G,

@@ -46,6 +46,7 @@
 // and no NaN.  The score scale (scale * k_scale * log2 e, positive) is folded
 // into the exponent's fused multiply-add.  E4M3 codes become bf16 in
 // registers (exact); v_scale is applied at the end.
+#include "common.h"
 #include "dispatch.h"
 
 namespace pa {
