@@ -107,11 +107,18 @@ struct PdSmem {
     struct {
       float m[PD_WAVES][G];
       float l[PD_WAVES][G];
-      float acc[PD_WAVES][G][D + 4];  // rows padded: no bank conflicts
+      // rows padded to a stride of 4 (mod 8) floats: the 16-byte deposits of 4
+      // lane rows x G heads conflict least there (SQ_LDS_BANK_CONFLICT per LDS
+      // instruction on the G = 8 workloads, stride 0 / 4 / 8 / 12 mod 32
+      // floats: 2.9 / 0.11 / 0.52 / 0.11)
+      float acc[PD_WAVES][G][D + 4];
     } area[T::HALVES][T::NPAR];
     struct {                          // ordering of the partial segments, before any merge
       int32_t cls[PD_SORT_MAX];
-      int32_t cnt[PD_SORT_MAX / 64][PD_SIZE_CLASSES];
+      // per chunk, class c at [c % (classes / 64)][c / (classes / 64)]: the
+      // scan's lane l, which owns a run of consecutive classes, then reads
+      // consecutive words with its neighbours
+      int32_t cnt[PD_SORT_MAX / 64][PD_SIZE_CLASSES / 64][64];
     } srt;
   } u;
 };
@@ -227,7 +234,7 @@ __global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_k
       }
     }
     const int nch = (NPART + 63) / 64;   // chunks holding entries
-    for (int i = tid; i < nch * NBK; i += NTH) (&sm.u.srt.cnt[0][0])[i] = 0;
+    for (int i = tid; i < nch * NBK; i += NTH) (&sm.u.srt.cnt[0][0][0])[i] = 0;
     __syncthreads();
     // entry e sits in chunk e / 64 (one wave's lanes); the lanes holding its
     // class are found bit-sliced (one ballot per bit of the 8-bit class), so
@@ -247,7 +254,7 @@ __global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_k
         same &= set ? bm : ~bm;
       }
       wr[r] = __builtin_popcountll(same & ((1ull << lane) - 1));
-      if (valid && wr[r] == 0) sm.u.srt.cnt[c][cls[r]] = __builtin_popcountll(same);
+      if (valid && wr[r] == 0) sm.u.srt.cnt[c][cls[r] % CPL][cls[r] / CPL] = __builtin_popcountll(same);
     }
     __syncthreads();
     // class starts (exclusive scan over classes of the chunk totals; lane l
@@ -256,7 +263,7 @@ __global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_k
     if (wave == 0) {
       int tot = 0;
       for (int k = 0; k < CPL; ++k)
-        for (int c = 0; c < nch; ++c) tot += sm.u.srt.cnt[c][CPL * lane + k];
+        for (int c = 0; c < nch; ++c) tot += sm.u.srt.cnt[c][k][lane];
       int x = tot;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -266,8 +273,8 @@ __global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_k
       int run = x - tot;
       for (int k = 0; k < CPL; ++k)
         for (int c = 0; c < nch; ++c) {
-          const int n = sm.u.srt.cnt[c][CPL * lane + k];
-          sm.u.srt.cnt[c][CPL * lane + k] = run;
+          const int n = sm.u.srt.cnt[c][k][lane];
+          sm.u.srt.cnt[c][k][lane] = run;
           run += n;
         }
     }
@@ -275,7 +282,7 @@ __global__ __launch_bounds__(64 * PD_WAVES * T::HALVES) void decode_persistent_k
 #pragma unroll
     for (int r = 0; r < SR; ++r)
       if (tid + r * NTH < NPART)
-        sm.plist[sm.u.srt.cnt[wave + r * (NTH / 64)][cls[r]] + wr[r]] = mine[r];
+        sm.plist[sm.u.srt.cnt[wave + r * (NTH / 64)][cls[r] % CPL][cls[r] / CPL] + wr[r]] = mine[r];
     __syncthreads();
   }
   if (tid < HV * NPAR) {

@@ -57,7 +57,12 @@ struct MfmaTile {
   // register buffers: NBUF - 1 sub-tiles in flight while one is computed
   // (E4M3 sub-tiles are half the bytes, so twice as many)
   static constexpr int NBUF = KV == KV_FP8 ? 5 : 3;
-  static constexpr int QROWB = (D + 8) * 2;    // staged query row (padded: no bank conflicts)
+  // staged query row: 16 bf16 of padding make the row stride 8 (mod 32)
+  // dwords, the stride at which set_query's 16-byte reads of 8 heads x 4 lane
+  // rows met the fewest LDS bank conflicts (strides of 0 / 4 / 8 / 12 / 16
+  // mod 32 dwords, SQ_LDS_BANK_CONFLICT per LDS instruction on the G = 8
+  // workloads: 0.56 / 0.11 / 0.026 / 0.11 / 0.026)
+  static constexpr int QROWB = (D + 16) * 2;
   static constexpr int QBYTES = G == 8 ? 57344 : G > 8 ? 32768 : 65536;
   static constexpr int NPAR = G <= 8 ? 2 : 1;  // merge areas that fit next to the rest
   static constexpr int HALVES = 2;             // two 4-wave halves per workgroup
