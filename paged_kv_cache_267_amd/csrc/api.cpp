@@ -247,6 +247,9 @@ int pa_extend(const void* query, const void* key_cache, const void* value_cache,
   if (num_tokens > (1 << 26)) return PA_ERR_SHAPE;  // column indices (token x head) stay in int
   if (num_tokens > 0 && max_query_len == 0) return PA_ERR_SHAPE;
   if ((long long)num_tokens * num_q_heads * head_dim >= (1ll << 40)) return PA_ERR_SHAPE;
+  // one physical block of the cache (every KV head) is addressed with 32 bits
+  if ((long long)num_kv_heads * head_dim * block_size * elem_bytes(kv_dtype) >= (1ll << 32))
+    return PA_ERR_SHAPE;
   if (!aligned16(out)) return PA_ERR_ALIGN;
   const int G = num_q_heads / num_kv_heads;
   const long long pairs = (long long)num_seqs * num_kv_heads;

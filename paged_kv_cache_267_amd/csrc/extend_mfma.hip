@@ -199,69 +199,111 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
   const bf16x8_t ones = as_bf16x8(BF16_ONE_X2, BF16_ONE_X2, BF16_ONE_X2, BF16_ONE_X2);
   const float qk = p.qk_scale;
   const size_t tile = (size_t)D * BS * T::E;  // bytes of one (block, head) tile
+  // The query operands are in registers before the first DMA load is issued:
+  // from here on the only vector-memory loads in flight are the ring's, so
+  // every wait in the loop can leave the later steps' loads in flight (a
+  // wait for a load issued before them would drain them all, vmcnt retiring
+  // in order).
+  wait_vmcnt<0>();
 
-  // Block-table entries of a 64-block window, one per lane: a step's block
-  // ids come from a lane read, not from memory, so no step waits on a load
-  // issued after the DMA loads still in flight (vmcnt retires in order).
-  // Moving the window (every 64 blocks) waits for them once.
-  int tb_base = -64, tb = 0;
-  auto block_id = [&](int bi) -> int {
-    const int base = bi & ~63;
-    if (base != tb_base) {
-      tb_base = base;
-      tb = row_bt[min(base + lane, p.max_blocks - 1)];
-    }
-    const int b = __builtin_amdgcn_readlane(tb, bi - base);
-    return min(max(b, 0), p.num_blocks - 1);
-  };
+  // Block ids come from scalar loads of the table (read-only for the whole
+  // launch, hence the constant address space), issued a step before they
+  // are needed; scalar loads are counted apart from the vector loads, so
+  // using them never waits on the ring.
+  typedef const __attribute__((address_space(4))) int32_t cbt_t;
+  cbt_t* sbt = (cbt_t*)row_bt;
+  auto block_id = [&](int bi) -> int { return sbt[min(bi, p.max_blocks - 1)]; };
+  auto clamp_id = [&](int b) -> int { return min(max(b, 0), p.num_blocks - 1); };
 
   // This wave's fragments of a step are slots wave*FW .. wave*FW+FW-1 of the
   // stage (K fragments first, then V).  Per lane: the step's base address,
   // plus a per-fragment offset.
   const bool moves_k = wave * FW < KF;
-  auto step_src = [&](int step) -> const char* {
-    const int key0 = (kq0 + step) * 32;
-    const int bi = min(key0 / BS, p.max_blocks - 1);
+  // the block ids of a step's 32 keys (two 16-token blocks, else one)
+  struct StepIds { int b0, b1; };
+  auto ids_of = [&](int step) -> StepIds {
+    const int bi = min((kq0 + step) * 32 / BS, p.max_blocks - 1);
     const int b0 = block_id(bi);
-    int b1 = b0;
-    if (BS == 16) b1 = block_id(min(bi + 1, p.max_blocks - 1));
+    return {b0, BS == 16 ? block_id(bi + 1) : b0};
+  };
+  // A lane's source address in a step is a fixed part, set here once, plus
+  // the block id times the block stride, plus (64-token blocks) the step's
+  // half of the block times the bytes one key position advances; with
+  // 16-token blocks a lane reads the step's first or second block.
+  //   K:        lane (r, c) takes key 8(c/4) + c%4 (+4), group r (+4i)
+  //   bf16 V:   dims 16v + c, keys 8r .. 8r+7
+  //   E4M3 V:   dims 32v + 16(r/2) + c, keys 16(r%2) .. +15
+  const uint32_t bstride = (uint32_t)(p.num_kv_heads * tile);   // below 2^32 (host check)
+  const char* lane_base;
+  bool lane_b1;
+  int key_bytes;
+  {
     const size_t head = (size_t)hk * tile;
-    if (moves_k) {  // K: lane (r, c) takes key 8(c/4) + c%4 (+4), group r (+4i)
+    if (moves_k) {
       const int kk = 8 * (c >> 2) + (c & 3);
-      const int blk = (BS == 16 && kk >= 16) ? b1 : b0;
-      return p.kc + (size_t)blk * p.num_kv_heads * tile + head + (r * BS + (key0 + kk) % BS) * 16;
+      lane_b1 = BS == 16 && kk >= 16;
+      lane_base = p.kc + head + (r * BS + (BS == 16 ? kk % 16 : kk)) * 16;
+      key_bytes = 16;
+    } else if (KV == KV_BF16) {
+      lane_b1 = BS == 16 && r >= 2;
+      lane_base = p.vc + head + (c * BS + (BS == 16 ? (8 * r) % 16 : 8 * r)) * 2;
+      key_bytes = 2;
+    } else {
+      lane_b1 = BS == 16 && (r & 1);
+      lane_base = p.vc + head + ((16 * (r >> 1) + c) * BS + (BS == 16 ? 0 : 16 * (r & 1)));
+      key_bytes = 1;
     }
-    if (KV == KV_BF16) {  // V: dims 16v + c, keys 8r .. 8r+7
-      const int blk = (BS == 16 && r >= 2) ? b1 : b0;
-      return p.vc + (size_t)blk * p.num_kv_heads * tile + head + (c * BS + (key0 + 8 * r) % BS) * 2;
-    }
-    // E4M3 V: dims 32v + 16(r/2) + c, keys 16(r%2) .. +15
-    const int blk = (BS == 16 && (r & 1)) ? b1 : b0;
-    return p.vc + (size_t)blk * p.num_kv_heads * tile + head +
-           ((16 * (r >> 1) + c) * BS + (key0 + 16 * (r & 1)) % BS);
+  }
+  auto step_src = [&](int step, StepIds ids) -> const char* {
+    // clamped here, at use, so the loads of the ids stay in flight until then
+    const int b0 = clamp_id(ids.b0), b1 = clamp_id(ids.b1);
+    const uint32_t blk = (uint32_t)(lane_b1 ? b1 : b0);
+    const int in_block = BS == 64 ? ((kq0 + step) * 32) % 64 : 0;
+    return lane_base + (uint64_t)blk * bstride + in_block * key_bytes;
   };
-  auto frag_off = [&](int jj) -> int {
-    const int f = wave * FW + jj;
-    if (moves_k) return (f / KL) * 64 + (f % KL) * 4 * BS * 16;
-    const int v = f - KF;
-    return KV == KV_BF16 ? v * 16 * BS * 2 : v * 32 * BS;
-  };
+  // byte offsets of this wave's fragments from its source address (uniform)
+  int frag_offs[FW];
+#pragma unroll
+  for (int jj = 0; jj < FW; ++jj) {
+    const int f = wave * FW + jj, v = f - KF;
+    frag_offs[jj] = moves_k ? (f / KL) * 64 + (f % KL) * 4 * BS * 16
+                            : (KV == KV_BF16 ? v * 16 * BS * 2 : v * 32 * BS);
+  }
+  auto frag_off = [&](int jj) -> int { return frag_offs[jj]; };
   auto slot = [&](int st, int jj) -> char* { return ring + st * T::STAGE + (wave * FW + jj) * 1024; };
 
   // DMA this wave's share of step `step` into stage `st`
-  auto fetch = [&](int step, int st) {
+  auto fetch = [&](int step, int st, StepIds ids) {
     if (wave >= NFW) return;
-    const char* src = step_src(step);
+    const char* src = step_src(step, ids);
 #pragma unroll
     for (int jj = 0; jj < FW; ++jj)
       __builtin_amdgcn_global_load_lds((const void*)(src + frag_off(jj)),
                                        (lds_void_t*)slot(st, jj), 16, 0, 0);
   };
+  // ids of the next step to fetch, loaded one fetch ahead
+  StepIds next_ids = {0, 0};
   if (nsteps > 0) {
 #pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i) fetch(min(i, nsteps - 1), i);
+    for (int i = 0; i < NBUF - 1; ++i) fetch(min(i, nsteps - 1), i, ids_of(min(i, nsteps - 1)));
+    next_ids = ids_of(min(NBUF - 1, nsteps - 1));
   }
+  // fetch step `ahead` with the ids loaded in the step before
+  auto fetch_ahead = [&](int ahead, int st) { fetch(ahead, st, next_ids); };
+  // At the end of step `step`, once its LDS reads are consumed, load the ids
+  // the next step fetches: scalar loads share a counter with LDS reads, so
+  // issued earlier they would make the step's LDS waits wait for them too.
+  // The barrier at the top of the next step waits for them.
+  auto load_next_ids = [&](int step) {
+    asm volatile("" ::: "memory");
+    next_ids = ids_of(min(step + NBUF, nsteps - 1));
+  };
 
+  int cur_st = 0, ahead_st = NBUF - 1;   // stage of `step`, and of the step fetched in it
+  auto next_stages = [&]() {
+    cur_st = cur_st == NBUF - 1 ? 0 : cur_st + 1;
+    ahead_st = ahead_st == NBUF - 1 ? 0 : ahead_st + 1;
+  };
   for (int step = 0; step < nsteps; ++step) {
     // this wave's share of `step` has landed; after the barrier everyone's
     // has, and every wave is done with the stage read one step earlier.  The
@@ -271,14 +313,16 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
     ring_barrier();
     // the stage to refill NBUF - 1 steps ahead (past the end the last step
     // is fetched again: the count of loads in flight stays fixed)
-    const int ahead = min(step + NBUF - 1, nsteps - 1), ahead_st = (step + NBUF - 1) % NBUF;
+    const int ahead = min(step + NBUF - 1, nsteps - 1);
 
     const int key0 = (kq0 + step) * 32;
     if (key0 + 32 <= klo || key0 >= khi) {  // no key of this wave's columns
-      fetch(ahead, ahead_st);
+      fetch_ahead(ahead, ahead_st);
+      load_next_ids(step);
+      next_stages();
       continue;
     }
-    const char* stage = ring + (step % NBUF) * T::STAGE;
+    const char* stage = ring + cur_st * T::STAGE;
 
     // K operands of both sub-tiles (E4M3 -> bf16 in registers)
     bf16x8_t kop[2][KS];
@@ -313,7 +357,7 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
     }
 
     // refill while the score products run
-    fetch(ahead, ahead_st);
+    fetch_ahead(ahead, ahead_st);
 
     // V operands: dword w holds keys 8r + 2w, 8r + 2w + 1 of dim 16nb + c
     uint32_t vq[NB][4];
@@ -390,6 +434,8 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
         acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             as_bf16x8(vq[nb][0], vq[nb][1], vq[nb][2], vq[nb][3]), pop[j], acc[j][nb], 0, 0, 0);
     }
+    load_next_ids(step);
+    next_stages();
   }
   // no DMA may still be writing this workgroup's LDS when it ends
   wait_vmcnt<0>();
