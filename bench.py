@@ -48,8 +48,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 def family_sources(family: str, names) -> list:
     """The device sources a kernel family is built from: the extend kernel's
     file, or the decode driver, its tiles and instances; both include
-    common.h and are launched through dispatch.*"""
-    shared = ("common.h", "dispatch.h", "dispatch.cpp")
+    common.h and params.h and are launched through dispatch.*"""
+    shared = ("common.h", "params.h", "dispatch.h", "dispatch.cpp")
     if family == "extend":
         return [f for f in names if f == "extend_mfma.hip" or f in shared]
     return [f for f in names if f.startswith(("decode_", "tile_")) or f in shared]
