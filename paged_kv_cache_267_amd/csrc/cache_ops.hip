@@ -9,33 +9,40 @@ namespace pa {
 // chenxutan.com, s2.1: a request's tokens fill ceil(n/bs) fixed-size blocks;
 // "vLLM deployment and PagedAttention", crazysre.cn, "Core concept": the block
 // table maps them to physical blocks).  One thread per (token, head, 16-byte
-// K group): the K group is one 16-byte store (it is contiguous in the cache);
-// the same X elements of V go to X rows of the V tile (stride bs elements).
+// K group), the head on blockIdx.y: the K group is one 16-byte store (it is
+// contiguous in the cache); the same X elements of V go to X rows of the V
+// tile (stride bs elements).  Token fastest: neighbouring lanes take
+// neighbouring tokens, whose slots are usually neighbours in one block (a
+// chunk of new tokens), so their K groups and V elements land side by side.
+// A launch covers tokens t_base .. t_base + nt - 1 (nt * groups <= 2^30) and
+// heads h_base + blockIdx.y.  The source row does not depend on the slot, so
+// its loads are issued together with the slot's: one memory round trip.
 template <int E>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const uint8_t* __restrict__ key, const uint8_t* __restrict__ value,
     uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, const int32_t* __restrict__ slots,
-    int num_tokens, int Hkv, int D, int bs, long long num_slots) {
+    int nt, int t_base, int h_base, int Hkv, int D, int bs, long long num_slots) {
   constexpr int X = 16 / E;
   const int groups = D / X;
-  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long total = (long long)num_tokens * Hkv * groups;
-  if (gid >= total) return;
-  // token fastest: neighbouring lanes take neighbouring tokens, whose slots
-  // are usually neighbours in one block (a chunk of new tokens), so the
-  // 16-byte K groups and the V elements of a row land side by side
-  const int t = (int)(gid % num_tokens);
-  const int grp = (int)((gid / num_tokens) % groups);
-  const int h = (int)(gid / ((long long)num_tokens * groups));
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i >= nt * groups) return;
+  const int t = t_base + (int)((unsigned)i % (unsigned)nt);
+  const int grp = (int)((unsigned)i / (unsigned)nt);
+  const int h = h_base + (int)blockIdx.y;
+  const size_t src = (((size_t)t * Hkv + h) * D + (size_t)grp * X) * E;
   const int slot = slots[t];
+  const u32x4_t kk = *(const u32x4_t*)(key + src);
+  const u32x4_t vv = *(const u32x4_t*)(value + src);
+  // a use before the slot test keeps the source loads ahead of it: otherwise
+  // the compiler moves them (or all but one dword of them) behind the test and
+  // the thread waits twice
+  asm volatile("" ::"v"(kk), "v"(vv));
   if (slot < 0 || (long long)slot >= num_slots) return;
   const int b = slot / bs, o = slot % bs;
-  const size_t src = (((size_t)t * Hkv + h) * D + (size_t)grp * X) * E;
   const size_t tile = ((size_t)b * Hkv + h) * (size_t)D * bs * E;
   // key: 16 contiguous bytes at group grp, token o
-  *(uint4*)(kc + tile + ((size_t)grp * bs + o) * 16) = *(const uint4*)(key + src);
+  *(u32x4_t*)(kc + tile + ((size_t)grp * bs + o) * 16) = kk;
   // value: element d goes to row d, column o
-  const uint4 vv = *(const uint4*)(value + src);
   const uint8_t* vb = (const uint8_t*)&vv;
 #pragma unroll
   for (int x = 0; x < X; ++x) {
@@ -75,28 +82,33 @@ template <int SE>
 __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
     const uint8_t* __restrict__ key, const uint8_t* __restrict__ value,
     uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, const int32_t* __restrict__ slots,
-    int num_tokens, int Hkv, int D, int bs, long long num_slots, float k_scale, float v_scale) {
+    int nt, int t_base, int h_base, int Hkv, int D, int bs, long long num_slots, float k_scale,
+    float v_scale) {
   const int groups = D / 16;
-  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long total = (long long)num_tokens * Hkv * groups;
-  if (gid >= total) return;
-  // token fastest: neighbouring lanes take neighbouring tokens, whose slots
-  // are usually neighbours in one block (a chunk of new tokens), so the
-  // 16-byte K groups and the V elements of a row land side by side
-  const int t = (int)(gid % num_tokens);
-  const int grp = (int)((gid / num_tokens) % groups);
-  const int h = (int)(gid / ((long long)num_tokens * groups));
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i >= nt * groups) return;
+  // token fastest, the head on blockIdx.y, as in reshape_and_cache_kernel
+  const int t = t_base + (int)((unsigned)i % (unsigned)nt);
+  const int grp = (int)((unsigned)i / (unsigned)nt);
+  const int h = h_base + (int)blockIdx.y;
+  const size_t src = (((size_t)t * Hkv + h) * D + (size_t)grp * 16) * SE;
+  u32x4_t kr[SE], vr[SE];   // the 16 source elements, 16 bytes at a time
   const int slot = slots[t];
+#pragma unroll
+  for (int c = 0; c < SE; ++c) {
+    kr[c] = *(const u32x4_t*)(key + src + 16 * c);
+    vr[c] = *(const u32x4_t*)(value + src + 16 * c);
+  }
+#pragma unroll
+  for (int c = 0; c < SE; ++c) asm volatile("" ::"v"(kr[c]), "v"(vr[c]));  // as above
   if (slot < 0 || (long long)slot >= num_slots) return;
   const int b = slot / bs, o = slot % bs;
-  const size_t src = (((size_t)t * Hkv + h) * D + (size_t)grp * 16) * SE;
   const size_t tile = ((size_t)b * Hkv + h) * (size_t)D * bs;
   float xk[16], xv[16];
 #pragma unroll
-  for (int c = 0; c < 16 * SE / 16; ++c) {   // 16-byte pieces of the 16 source elements
-    const uint4 k4 = *(const uint4*)(key + src + 16 * c);
-    const uint4 v4 = *(const uint4*)(value + src + 16 * c);
-    const uint32_t kw[4] = {k4.x, k4.y, k4.z, k4.w}, vw[4] = {v4.x, v4.y, v4.z, v4.w};
+  for (int c = 0; c < SE; ++c) {
+    const uint32_t kw[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
+    const uint32_t vw[4] = {vr[c].x, vr[c].y, vr[c].z, vr[c].w};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       if (SE == 4) {
@@ -242,26 +254,45 @@ __global__ __launch_bounds__(256) void fp8_dequant_kernel(const uint8_t* __restr
   for (int k = 0; k < 4 && i + k < n; ++k) out[i + k] = v[k] * scale;
 }
 
+// Launches of an append, in chunks that keep the kernels' 32-bit indices in
+// range: at most RC_TOKENS tokens (times at most 32 groups <= 2^30 threads)
+// and RC_HEADS heads (grid y) per launch.  One launch for any realistic call.
+constexpr int RC_TOKENS = 1 << 25;
+constexpr int RC_HEADS = 32768;
+
+template <class F>
+static hipError_t for_each_chunk(int T, int Hkv, int groups, F launch) {
+  for (long long t0 = 0; t0 < T; t0 += RC_TOKENS) {
+    const int nt = (int)min((long long)RC_TOKENS, T - t0);
+    const unsigned bx = (unsigned)(((long long)nt * groups + 255) / 256);
+    for (long long h0 = 0; h0 < Hkv; h0 += RC_HEADS) {
+      launch(dim3(bx, (unsigned)min((long long)RC_HEADS, Hkv - h0)), nt, (int)t0, (int)h0);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc, void* vc,
                                     const int32_t* slots, int T, int Hkv, int D, int bs,
                                     int num_blocks, int elem_bytes, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
   const int groups = D * elem_bytes / 16;
-  const long long total = (long long)T * Hkv * groups;
-  if (total == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((total + 255) / 256);
   const long long nslots = (long long)num_blocks * bs;
   const uint8_t *k8 = (const uint8_t*)key, *v8 = (const uint8_t*)value;
   uint8_t *kc8 = (uint8_t*)kc, *vc8 = (uint8_t*)vc;
-  if (elem_bytes == 4)
-    hipLaunchKernelGGL(reshape_and_cache_kernel<4>, dim3(blocks), dim3(256), 0, stream, k8, v8,
-                       kc8, vc8, slots, T, Hkv, D, bs, nslots);
-  else if (elem_bytes == 2)
-    hipLaunchKernelGGL(reshape_and_cache_kernel<2>, dim3(blocks), dim3(256), 0, stream, k8, v8,
-                       kc8, vc8, slots, T, Hkv, D, bs, nslots);
-  else
-    hipLaunchKernelGGL(reshape_and_cache_kernel<1>, dim3(blocks), dim3(256), 0, stream, k8, v8,
-                       kc8, vc8, slots, T, Hkv, D, bs, nslots);
-  return hipGetLastError();
+  return for_each_chunk(T, Hkv, groups, [&](dim3 grid, int nt, int t0, int h0) {
+    if (elem_bytes == 4)
+      hipLaunchKernelGGL(reshape_and_cache_kernel<4>, grid, dim3(256), 0, stream, k8, v8, kc8,
+                         vc8, slots, nt, t0, h0, Hkv, D, bs, nslots);
+    else if (elem_bytes == 2)
+      hipLaunchKernelGGL(reshape_and_cache_kernel<2>, grid, dim3(256), 0, stream, k8, v8, kc8,
+                         vc8, slots, nt, t0, h0, Hkv, D, bs, nslots);
+    else
+      hipLaunchKernelGGL(reshape_and_cache_kernel<1>, grid, dim3(256), 0, stream, k8, v8, kc8,
+                         vc8, slots, nt, t0, h0, Hkv, D, bs, nslots);
+  });
 }
 
 template <bool OUT_BF16, int D, int WPR>
@@ -294,19 +325,18 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void
                                         const int32_t* slots, int T, int Hkv, int D, int bs,
                                         int num_blocks, int src_bytes, float k_scale,
                                         float v_scale, hipStream_t stream) {
-  const long long total = (long long)T * Hkv * (D / 16);
-  if (total == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (T == 0) return hipSuccess;
   const long long nslots = (long long)num_blocks * bs;
   const uint8_t *k8 = (const uint8_t*)key, *v8 = (const uint8_t*)value;
   uint8_t *kc8 = (uint8_t*)kc, *vc8 = (uint8_t*)vc;
-  if (src_bytes == 4)
-    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<4>, dim3(blocks), dim3(256), 0, stream, k8,
-                       v8, kc8, vc8, slots, T, Hkv, D, bs, nslots, k_scale, v_scale);
-  else
-    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<2>, dim3(blocks), dim3(256), 0, stream, k8,
-                       v8, kc8, vc8, slots, T, Hkv, D, bs, nslots, k_scale, v_scale);
-  return hipGetLastError();
+  return for_each_chunk(T, Hkv, D / 16, [&](dim3 grid, int nt, int t0, int h0) {
+    if (src_bytes == 4)
+      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<4>, grid, dim3(256), 0, stream, k8, v8,
+                         kc8, vc8, slots, nt, t0, h0, Hkv, D, bs, nslots, k_scale, v_scale);
+    else
+      hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<2>, grid, dim3(256), 0, stream, k8, v8,
+                         kc8, vc8, slots, nt, t0, h0, Hkv, D, bs, nslots, k_scale, v_scale);
+  });
 }
 
 hipError_t launch_reduce_lse(const float* part_out, const float* part_lse,
