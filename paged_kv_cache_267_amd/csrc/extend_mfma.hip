@@ -26,7 +26,10 @@
 // not need.  Column blocks of one (sequence, KV head) are dealt to one XCD
 // (workgroup j runs on XCD j % 8) so that they share its L2, pairs round
 // robin over the XCDs, the last column block of a pair (the most keys,
-// causally) first.
+// causally) first.  With at most 64 sequences, pairs are dealt in order of
+// their sequence's work (attended keys summed over its new tokens), largest
+// first, so that the last workgroups to start are short ones; every wave
+// ranks the sequences itself, one lane per sequence.
 //
 // Per step and column block of 16 columns (v_mfma_f32_16x16x32_bf16 for both
 // products, heads/tokens on N):
@@ -98,6 +101,53 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Sequences ranked by work before dealing (at most one per lane).
+constexpr int EX_RANKED_SEQS = 64;
+
+// A sequence's length (clamped to the table's capacity) and its rows of new
+// tokens, clamped as the kernel uses them.
+struct ExSeq { int L, q0, n; };
+__device__ __forceinline__ ExSeq ex_seq(const ExtendParams& p, int s, int Lmax) {
+  const int L = min(max(p.seq_lens[s], 0), Lmax);
+  const int q0 = min(max(p.qsl[s], 0), p.num_tokens);
+  const int q1 = min(max(p.qsl[s + 1], q0), p.num_tokens);
+  return {L, q0, q1 - q0};
+}
+
+// Work of a sequence: keys attended summed over its n new tokens (token i
+// at position L - n + i attends min(L - n + i + 1, W) keys; W = 0: no
+// window).  Float: only the order matters.
+__device__ __forceinline__ float ex_seq_work(ExSeq q, int window) {
+  const float a = (float)(q.L - q.n + 1), b = (float)q.L;   // keys of the first and last token
+  if (q.n <= 0 || b <= 0.f) return 0.f;
+  const float W = (float)window;
+  if (window <= 0 || b <= W) return 0.5f * (float)q.n * (fmaxf(a, 1.f) + b);
+  if (a >= W) return (float)q.n * W;
+  // tokens below the window's width, then the rest at W keys each
+  const float below = W - a;
+  return 0.5f * below * (a + W - 1.f) + ((float)q.n - below) * W;
+}
+
+// The sequence of rank r when sequences are ordered by work, largest first
+// (ties: lower index first), with its clamped length and rows.  Needs
+// num_seqs <= 64 (lane l reads sequence l); every lane returns the same.
+__device__ __forceinline__ ExSeq seq_of_rank(const ExtendParams& p, int r, int lane, int Lmax,
+                                             int& s_out) {
+  const int S = p.num_seqs;
+  const ExSeq mine = lane < S ? ex_seq(p, lane, Lmax) : ExSeq{0, 0, 0};
+  const float w = lane < S ? ex_seq_work(mine, p.window) : -1.f;
+  int rank = 0;
+  for (int t = 0; t < S; ++t) {
+    const float wt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), t));
+    rank += (wt > w || (wt == w && t < lane)) ? 1 : 0;
+  }
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < S && rank == r);
+  const int s = hit != 0 ? (int)__builtin_ctzll(hit) : r;
+  s_out = s;
+  return {__builtin_amdgcn_readlane(mine.L, s), __builtin_amdgcn_readlane(mine.q0, s),
+          __builtin_amdgcn_readlane(mine.n, s)};
+}
+
 template <int KV, int D, int BS, int NCB, int NBUF>
 struct ExtendTile {
   static constexpr int E = KvTraits<KV>::E;
@@ -128,18 +178,20 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
   const int lane = threadIdx.x & 63, r = lane >> 4, c = lane & 15;
   const int wave = wave_id();
 
-  // work item: XCD x takes pairs x, x + 8, ...; a pair's column blocks in a row
+  // work item: XCD x takes pairs x, x + 8, ... of the dealing order; a
+  // pair's column blocks in a row
   const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
   const int pair = x + 8 * (k / p.cblocks);
   if (pair >= p.pairs) return;
   const int cb = p.cblocks - 1 - k % p.cblocks;
-  const int s = pair / p.num_kv_heads, hk = pair % p.num_kv_heads;
+  const int hk = pair % p.num_kv_heads;
+  int s = pair / p.num_kv_heads;
+  const ExSeq sq = p.num_seqs <= EX_RANKED_SEQS
+                       ? seq_of_rank(p, pair / p.num_kv_heads, lane, p.max_blocks * BS, s)
+                       : ex_seq(p, s, p.max_blocks * BS);
   const int G = 1 << p.log2g;
 
-  const int L = min(max(p.seq_lens[s], 0), p.max_blocks * BS);
-  const int q0 = min(max(p.qsl[s], 0), p.num_tokens);
-  const int q1 = min(max(p.qsl[s + 1], q0), p.num_tokens);
-  const int n = q1 - q0;
+  const int L = sq.L, q0 = sq.q0, n = sq.n;
   const int ncols = n << p.log2g;
   const int wg_col0 = cb * EX_WAVES * CW;
   if (wg_col0 >= ncols) return;  // the whole workgroup leaves before any barrier
