@@ -87,6 +87,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Wave priority around the matrix-product regions (1) and the softmax (0):
+// when the two waves sharing a SIMD are ready together, the one issuing
+// products goes first, so their phases drift apart and one wave's softmax
+// fills the other's product latency (1-2 % on the prefill workloads).  The
+// scheduling barriers keep the compiler from moving work across the switch.
+template <int P>
+__device__ __forceinline__ void wave_priority() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(P);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Workgroup barrier for the LDS ring: this wave's LDS reads are complete
 // (lgkmcnt 0) and every wave has arrived.  No memory fence: a fence would
 // also wait for the DMA loads still in flight for later steps (they count
@@ -394,6 +406,7 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
       }
     const bool full = key0 >= lo_max && key0 + 32 <= hi_min && hi_min > 0;
 
+    wave_priority<1>();
     // scores of every column block first: the V reads below overlap them
     f32x4_t sacc[NCB][2];
 #pragma unroll
@@ -446,6 +459,7 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
 #pragma unroll
         for (int w2 = 0; w2 < 4; ++w2) vq[nb][w2] &= vmask[w2];
     }
+    wave_priority<0>();
     // Softmax in two phases.  First, per column block: mask, running max
     // and the lazy rescale (a rare branch).  Then one branch-free run: the
     // weights of block 0, then each block's P.V products interleaved with
@@ -489,6 +503,7 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
     // Region j (fenced by scheduling barriers): block j's NB + 1 products,
     // each followed by a share of block j+1's weight instructions.
     bf16x8_t pop = weights(0);
+    wave_priority<1>();
     if (KV == KV_BF16) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < NCB; ++j) {
@@ -512,6 +527,7 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
         pop = next;
       }
     }
+    wave_priority<0>();
     load_next_ids(step);
     next_stages();
   }
