@@ -53,6 +53,42 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   }
 }
 
+// The same write for appends of few tokens (decode: one token per sequence,
+// each in a block of its own), one thread per (token, head, element d) with
+// d fastest: the 64 lanes of a V store write 64 rows of one token, which
+// share D * E * bs / 128 cache lines instead of touching 64 lines of 64
+// blocks; threads d < D * E / 16 also write K group d.  A launch covers
+// tokens t_base .. t_base + nt - 1 (nt * D <= 2^30) and heads h_base +
+// blockIdx.y.
+template <int E>
+__global__ __launch_bounds__(256) void reshape_and_cache_rows_kernel(
+    const uint8_t* __restrict__ key, const uint8_t* __restrict__ value,
+    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, const int32_t* __restrict__ slots,
+    int nt, int t_base, int h_base, int Hkv, int D, int bs, long long num_slots) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i >= nt * D) return;
+  const int t = t_base + (int)((unsigned)i / (unsigned)D), d = (int)((unsigned)i % (unsigned)D);
+  const int h = h_base + (int)blockIdx.y;
+  const size_t row = ((size_t)t * Hkv + h) * D * E;
+  const bool kgroup = d < D * E / 16;
+  const int slot = slots[t];
+  uint32_t v;
+  if (E == 4) v = *(const uint32_t*)(value + row + 4 * d);
+  else if (E == 2) v = *(const uint16_t*)(value + row + 2 * d);
+  else v = value[row + d];
+  u32x4_t kk = {0u, 0u, 0u, 0u};
+  if (kgroup) kk = *(const u32x4_t*)(key + row + 16 * d);
+  asm volatile("" ::"v"(kk), "v"(v));   // the source loads stay ahead of the slot test
+  if (slot < 0 || (long long)slot >= num_slots) return;
+  const int b = slot / bs, o = slot % bs;
+  const size_t tile = ((size_t)b * Hkv + h) * (size_t)D * bs * E;
+  uint8_t* dst = vc + tile + ((size_t)d * bs + o) * E;
+  if (E == 4) *(uint32_t*)dst = v;
+  else if (E == 2) *(uint16_t*)dst = (uint16_t)v;
+  else *dst = (uint8_t)v;
+  if (kgroup) *(u32x4_t*)(kc + tile + ((size_t)d * bs + o) * 16) = kk;
+}
+
 // E4M3 code of a binary32 value: nearest code, ties to even, saturating at
 // +-448 (infinities included), NaN -> 0x7F.  Codes are (1 + m/8) * 2^(e-7) for
 // exponent field e >= 1 and m/8 * 2^-6 for e = 0.  Normal range: the fp32
@@ -255,7 +291,8 @@ __global__ __launch_bounds__(256) void fp8_dequant_kernel(const uint8_t* __restr
 }
 
 // Launches of an append, in chunks that keep the kernels' 32-bit indices in
-// range: at most RC_TOKENS tokens (times at most 32 groups <= 2^30 threads)
+// range: at most RC_TOKENS tokens (times at most 32 groups <= 2^30 threads;
+// the element-per-thread mapping only runs appends of a few thousand tokens)
 // and RC_HEADS heads (grid y) per launch.  One launch for any realistic call.
 constexpr int RC_TOKENS = 1 << 25;
 constexpr int RC_HEADS = 32768;
@@ -274,6 +311,12 @@ static hipError_t for_each_chunk(int T, int Hkv, int groups, F launch) {
   return hipSuccess;
 }
 
+// Appends of at most this many tokens take the element-per-thread mapping:
+// a decode step's tokens sit in blocks of their own, where it writes fewer,
+// fuller lines; longer appends are chunks whose neighbouring tokens share V
+// rows, which the token-per-lane mapping writes side by side.
+constexpr int RC_ROWS_MAX_TOKENS = 4096;
+
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc, void* vc,
                                     const int32_t* slots, int T, int Hkv, int D, int bs,
                                     int num_blocks, int elem_bytes, hipStream_t stream) {
@@ -282,6 +325,18 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc
   const long long nslots = (long long)num_blocks * bs;
   const uint8_t *k8 = (const uint8_t*)key, *v8 = (const uint8_t*)value;
   uint8_t *kc8 = (uint8_t*)kc, *vc8 = (uint8_t*)vc;
+  if (T <= RC_ROWS_MAX_TOKENS)
+    return for_each_chunk(T, Hkv, D, [&](dim3 grid, int nt, int t0, int h0) {
+      if (elem_bytes == 4)
+        hipLaunchKernelGGL(reshape_and_cache_rows_kernel<4>, grid, dim3(256), 0, stream, k8, v8,
+                           kc8, vc8, slots, nt, t0, h0, Hkv, D, bs, nslots);
+      else if (elem_bytes == 2)
+        hipLaunchKernelGGL(reshape_and_cache_rows_kernel<2>, grid, dim3(256), 0, stream, k8, v8,
+                           kc8, vc8, slots, nt, t0, h0, Hkv, D, bs, nslots);
+      else
+        hipLaunchKernelGGL(reshape_and_cache_rows_kernel<1>, grid, dim3(256), 0, stream, k8, v8,
+                           kc8, vc8, slots, nt, t0, h0, Hkv, D, bs, nslots);
+    });
   return for_each_chunk(T, Hkv, groups, [&](dim3 grid, int nt, int t0, int h0) {
     if (elem_bytes == 4)
       hipLaunchKernelGGL(reshape_and_cache_kernel<4>, grid, dim3(256), 0, stream, k8, v8, kc8,

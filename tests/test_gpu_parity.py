@@ -95,6 +95,24 @@ def test_reshape_and_cache_bit_exact(kvdt, D, bs):
     assert np.array_equal(gv, vc.view(np.uint8))
 
 
+@pytest.mark.parametrize("kvdt,D,bs", [("bf16", 128, 16), ("fp8_e4m3", 64, 32),
+                                       ("f32", 128, 64)])
+def test_reshape_and_cache_both_mappings_bit_exact(kvdt, D, bs):
+    """The history fill writes more than 4096 tokens (the token-per-lane
+    mapping) and the step's append a few (the element-per-thread mapping):
+    both land where the oracle puts them, in the same cache."""
+    announce(f"reshape_and_cache, long history {kvdt} D{D} bs{bs}")
+    qdt = "f32" if kvdt == "f32" else "bf16"
+    wl = W.random_case(22, seq_lens=[1, 17, 100, 2600, 3000], num_q_heads=4, num_kv_heads=2,
+                       head_dim=D, block_size=bs, q_dtype=qdt, kv_dtype=kvdt)
+    assert wl.hist_slots.shape[0] > 4096 and wl.new_slots.shape[0] <= 4096
+    dw = gpu_run(wl, split=False)
+    gk, gv = dw.cache_bytes()
+    kc, vc = oracle_caches(wl)
+    assert np.array_equal(gk, kc.view(np.uint8))
+    assert np.array_equal(gv, vc.view(np.uint8))
+
+
 def test_reshape_and_cache_skips_negative_and_out_of_pool_slots():
     import torch
     import paged_kv_cache_267_amd as pa
