@@ -218,6 +218,28 @@ def test_extend_small_parity(kvdt, D, bs, G, window):
     _assert_close(dw.out_f64(), ref, kvdt, f"extend kv={kvdt} D={D} bs={bs} G={G} W={window}")
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("nseq,kvdt,window", [(64, "bf16", 0), (65, "bf16", 0),
+                                              (64, "fp8_e4m3", 90), (65, "fp8_e4m3", 90)])
+def test_extend_dealing_orders(nseq, kvdt, window):
+    """Batches of up to 64 sequences are dealt by work (one lane per sequence
+    ranks them); larger batches in sequence order.  64 and 65 sequences run
+    both paths; equal (length, chunk) pairs make ties, broken by index."""
+    rng = np.random.default_rng(900 + nseq)
+    q = rng.integers(1, 40, size=nseq)
+    lens = q + rng.integers(0, 260, size=nseq)
+    lens[1::7], q[1::7] = lens[0], q[0]          # ties in work
+    q[2::11] = 1                                 # one-token chunks
+    _announce(f"extend dealing order: {nseq} sequences kv={kvdt} W={window}")
+    wl = W.random_case(950 + nseq, seq_lens=lens.tolist(), q_lens=q.tolist(), num_q_heads=8,
+                       num_kv_heads=2, head_dim=128, block_size=16, kv_dtype=kvdt,
+                       sliding_window=window)
+    kc, vc = oracle_caches(wl)
+    ref = oracle_extend(wl, kc, vc)
+    dw = _gpu_extend(wl)
+    _assert_close(dw.out_f64(), ref, kvdt, f"extend {nseq} sequences kv={kvdt} W={window}")
+
+
 def _sample_rows(wl, n, seed):
     total = wl.num_tokens * wl.num_q_heads
     rng = np.random.default_rng(seed)
