@@ -158,7 +158,8 @@ int pa_decode(const void* query, const void* key_cache, const void* value_cache,
  * [lo, L)); each partition is normalised on its own and reports its
  * log-sum-exp, so that pa_reduce_lse can merge them.
  * partition_size      a multiple of block_size (and of 16), > 0.
- * max_num_partitions  >= ceil(max_blocks_per_seq * block_size / partition_size).
+ * max_num_partitions  >= ceil(max_blocks_per_seq * block_size / partition_size),
+ *                     and at most 65535 (else PA_ERR_PARTITION).
  * part_out  fp32 [num_seqs][num_q_heads][max_num_partitions][head_dim]:
  *           softmax-weighted V of the partition (already divided by its sum).
  * part_lse  fp32 [num_seqs][num_q_heads][max_num_partitions]: natural-log
