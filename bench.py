@@ -187,6 +187,23 @@ def per_launch_us(fn, n: int, stream) -> float:
     return a.elapsed_time(b) * 1e3 / n
 
 
+def bracketed_launch_us(fn, n: int, stream) -> float:
+    """Average GPU duration of one launch of fn, with HIP events around each
+    launch.  For kernels of a few microseconds: launched back to back they
+    run at the host's launch rate, not at their own."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) * 1e3 / n
+
+
 def timed_steps(step, n: int, stream):
     """The timed region: n steps launched back to back, synchronised on both
     sides; returns (wall seconds, GPU event microseconds per step)."""
@@ -328,7 +345,7 @@ def run_extend(args):
         dw.step_extend()
     torch.cuda.synchronize()
     T, step_event_us = timed_steps(dw.step_extend, args.steps, stream)
-    t_app = per_launch_us(dw.append_new, args.steps, stream)
+    t_app = bracketed_launch_us(dw.append_new, args.steps, stream)
     t_ext = per_launch_us(dw.extend, args.steps, stream)
     graph = None
     if not args.no_graph:
@@ -352,8 +369,9 @@ def run_extend(args):
                               "event_per_step": round(step_event_us, 2),
                               "wall_per_step": round(ms_step * 1e3, 2)},
         "step_timing": ("K eager steps back to back on one stream (wall clock, synchronised on "
-                        "both sides); kernel times from K back-to-back launches of each kernel "
-                        "between two HIP events"),
+                        "both sides); the extend kernel's time from K back-to-back launches "
+                        "between two HIP events; the append's from HIP events around each of K "
+                        "launches (back to back its launches run at the host's rate)"),
         "graph": graph,
         "settle": settled,
         "flops_per_step": fl,
@@ -477,9 +495,9 @@ def main():
     # the timed region: K whole steps (append, attend, merge) back to back
     T, step_event_us = timed_steps(lambda: dw.step(split=split), args.steps, stream)
     # each kernel of the step on its own: K back-to-back launches
-    t_app = per_launch_us(dw.append_new, args.steps, stream)
+    t_app = bracketed_launch_us(dw.append_new, args.steps, stream)
     t_dec = per_launch_us(dw.decode_split if split else dw.decode_unsplit, args.steps, stream)
-    t_red = per_launch_us(dw.reduce, args.steps, stream) if split else 0.0
+    t_red = bracketed_launch_us(dw.reduce, args.steps, stream) if split else 0.0
 
     graph = None
     if not args.no_graph:
@@ -539,8 +557,10 @@ def main():
                               "event_per_step": round(step_event_us, 2),
                               "wall_per_step": round(ms_step * 1e3, 2)},
         "step_timing": ("K eager steps back to back on one stream (wall clock, synchronised on "
-                        "both sides); kernel times from K back-to-back launches of each kernel "
-                        "between two HIP events"),
+                        "both sides); the decode kernel's time from K back-to-back launches "
+                        "between two HIP events; the append's and the LSE merge's from HIP "
+                        "events around each of K launches (back to back their launches run at "
+                        "the host's rate)"),
         "graph": graph,
         "settle": settled,
         "kv_bytes_per_step": kv,
