@@ -187,21 +187,30 @@ def per_launch_us(fn, n: int, stream) -> float:
     return a.elapsed_time(b) * 1e3 / n
 
 
-def bracketed_launch_us(fn, n: int, stream) -> float:
-    """Average GPU duration of one launch of fn, with HIP events around each
-    launch.  For kernels of a few microseconds: launched back to back they
-    run at the host's launch rate, not at their own."""
+def queued_launch_us(fn, n: int, stream) -> tuple:
+    """Average GPU duration of one launch of fn for kernels of a few
+    microseconds, which back to back would run at the host's launch rate:
+    the n launches are queued behind a head start of device fills, so the GPU
+    meets them already enqueued and runs them back to back.  Returns (us per
+    launch, whether the host had enqueued all n before the GPU reached them)."""
     import torch
     fn()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n)]
-    for a, b in ev:
-        a.record(stream)
+    pad = torch.empty(64 << 20, dtype=torch.float32, device="cuda")   # 256 MiB
+    h0, h1, a, b = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    h0.record(stream)
+    for _ in range(max(8, n // 2)):
+        pad.fill_(1.0)
+    h1.record(stream)
+    a.record(stream)
+    t0 = time.perf_counter()
+    for _ in range(n):
         fn()
-        b.record(stream)
+    host_us = (time.perf_counter() - t0) * 1e6
+    b.record(stream)
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in ev) * 1e3 / n
+    del pad
+    return a.elapsed_time(b) * 1e3 / n, host_us < h0.elapsed_time(h1) * 1e3
 
 
 def timed_steps(step, n: int, stream):
@@ -345,7 +354,7 @@ def run_extend(args):
         dw.step_extend()
     torch.cuda.synchronize()
     T, step_event_us = timed_steps(dw.step_extend, args.steps, stream)
-    t_app = bracketed_launch_us(dw.append_new, args.steps, stream)
+    t_app, q_app = queued_launch_us(dw.append_new, args.steps, stream)
     t_ext = per_launch_us(dw.extend, args.steps, stream)
     graph = None
     if not args.no_graph:
@@ -367,11 +376,13 @@ def run_extend(args):
                    "seq_len_mean": float(wl.seq_lens.mean()), "parallelism": "single GPU"},
         "step_breakdown_us": {"reshape_and_cache": round(t_app, 2), "extend": round(t_ext, 2),
                               "event_per_step": round(step_event_us, 2),
-                              "wall_per_step": round(ms_step * 1e3, 2)},
+                              "wall_per_step": round(ms_step * 1e3, 2),
+                              "short_kernels_queued": q_app},
         "step_timing": ("K eager steps back to back on one stream (wall clock, synchronised on "
                         "both sides); the extend kernel's time from K back-to-back launches "
-                        "between two HIP events; the append's from HIP events around each of K "
-                        "launches (back to back its launches run at the host's rate)"),
+                        "between two HIP events; the append's from K launches queued behind "
+                        "device fills, so that they run back to back at the GPU's rate, not the "
+                        "host's"),
         "graph": graph,
         "settle": settled,
         "flops_per_step": fl,
@@ -495,9 +506,9 @@ def main():
     # the timed region: K whole steps (append, attend, merge) back to back
     T, step_event_us = timed_steps(lambda: dw.step(split=split), args.steps, stream)
     # each kernel of the step on its own: K back-to-back launches
-    t_app = bracketed_launch_us(dw.append_new, args.steps, stream)
+    t_app, q_app = queued_launch_us(dw.append_new, args.steps, stream)
     t_dec = per_launch_us(dw.decode_split if split else dw.decode_unsplit, args.steps, stream)
-    t_red = bracketed_launch_us(dw.reduce, args.steps, stream) if split else 0.0
+    t_red, q_red = queued_launch_us(dw.reduce, args.steps, stream) if split else (0.0, True)
 
     graph = None
     if not args.no_graph:
@@ -555,12 +566,13 @@ def main():
         "step_breakdown_us": {"reshape_and_cache": round(t_app, 2), "decode": round(t_dec, 2),
                               "reduce_lse": round(t_red, 2),
                               "event_per_step": round(step_event_us, 2),
-                              "wall_per_step": round(ms_step * 1e3, 2)},
+                              "wall_per_step": round(ms_step * 1e3, 2),
+                              "short_kernels_queued": bool(q_app and q_red)},
         "step_timing": ("K eager steps back to back on one stream (wall clock, synchronised on "
                         "both sides); the decode kernel's time from K back-to-back launches "
-                        "between two HIP events; the append's and the LSE merge's from HIP "
-                        "events around each of K launches (back to back their launches run at "
-                        "the host's rate)"),
+                        "between two HIP events; the append's and the LSE merge's from K "
+                        "launches queued behind device fills, so that they run back to back at "
+                        "the GPU's rate, not the host's"),
         "graph": graph,
         "settle": settled,
         "kv_bytes_per_step": kv,
