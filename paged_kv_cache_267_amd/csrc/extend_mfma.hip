@@ -447,13 +447,16 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
     // keys outside [klo, khi) may be unwritten or outside the window's
     // blocks: zero their V so that p = 0 never meets a NaN
     if (key0 < klo || key0 + 32 > khi) {
+      // key key0 + 8r + i is kept when i is in [vlo, vhi): offsets against
+      // constants, so no per-key index is formed outside the masked steps
+      int k0 = key0;
+      asm("" : "+s"(k0));   // formed here: not an induction variable of every step
+      const int vlo = klo - k0 - 8 * r, vhi = khi - k0 - 8 * r;
       uint32_t vmask[4];
 #pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) {
-        const int kk = key0 + 8 * r + 2 * w2;
-        vmask[w2] = ((kk >= klo && kk < khi) ? 0xffffu : 0u) |
-                    ((kk + 1 >= klo && kk + 1 < khi) ? 0xffff0000u : 0u);
-      }
+      for (int w2 = 0; w2 < 4; ++w2)
+        vmask[w2] = ((2 * w2 >= vlo && 2 * w2 < vhi) ? 0xffffu : 0u) |
+                    ((2 * w2 + 1 >= vlo && 2 * w2 + 1 < vhi) ? 0xffff0000u : 0u);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -473,12 +476,13 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
       float* sc = scs[j];
       sc[0] = s0[0]; sc[1] = s0[1]; sc[2] = s0[2]; sc[3] = s0[3];
       sc[4] = s1[0]; sc[5] = s1[1]; sc[6] = s1[2]; sc[7] = s1[3];
-      if (!full) {
+      if (!full) {   // key key0 + 8r + i is in [lo_c, hi_c) when i is in [slo, shi)
+        int k0 = key0;
+        asm("" : "+s"(k0));
+        const int slo = lo_c[j] - k0 - 8 * r, shi = hi_c[j] - k0 - 8 * r;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int key = key0 + 8 * r + i;
-          if (!(key >= lo_c[j] && key < hi_c[j])) sc[i] = -INFINITY;
-        }
+        for (int i = 0; i < 8; ++i)
+          if (!(i >= slo && i < shi)) sc[i] = -INFINITY;
       }
       float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                        fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
