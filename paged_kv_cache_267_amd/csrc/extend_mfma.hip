@@ -262,6 +262,10 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
   }
   const bf16x8_t ones = as_bf16x8(BF16_ONE_X2, BF16_ONE_X2, BF16_ONE_X2, BF16_ONE_X2);
   const float qk = p.qk_scale;
+  // a raw score above thr[j] would put its weight above 2^EX_LAZY_LOG2 (qk > 0)
+  float thr[NCB];
+#pragma unroll
+  for (int j = 0; j < NCB; ++j) thr[j] = (m_ref[j] + EX_LAZY_LOG2) / qk;
   const size_t tile = (size_t)D * BS * T::E;  // bytes of one (block, head) tile
   // The query operands are in registers before the first DMA load is issued:
   // from here on the only vector-memory loads in flight are the ring's, so
@@ -484,16 +488,24 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
         for (int i = 0; i < 8; ++i)
           if (!(i >= slo && i < shi)) sc[i] = -INFINITY;
       }
-      float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                       fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-      mx = ex_colmax4(mx) * qk;
-      if (__builtin_amdgcn_ballot_w64(mx > m_ref[j] + EX_LAZY_LOG2) != 0) {
+      // Lazy rescale: only a score above its column's threshold calls for
+      // one, so a step compares its scores and forms the column max (and the
+      // new reference) only when some lane finds one.  Scaling by qk > 0 keeps
+      // the order, so this is the test "column max * qk > m_ref + 2^LAZY".
+      bool over = false;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) over |= sc[i] > thr[j];
+      if (__builtin_amdgcn_ballot_w64(over) != 0) {
+        float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                         fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+        mx = ex_colmax4(mx) * qk;
         const float m_new = fmaxf(m_ref[j], mx);
         const float alpha = fast_exp2(m_ref[j] - m_new);
         accl[j] *= alpha;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[j][nb] *= alpha;
         m_ref[j] = m_new;
+        thr[j] = (m_new + EX_LAZY_LOG2) / qk;
       }
     }
     auto weights = [&](int j) -> bf16x8_t {
