@@ -323,21 +323,23 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
     }
   }
   auto step_src = [&](int step, StepIds ids) -> const char* {
-    // clamped here, at use, so the loads of the ids stay in flight until then
-    const int b0 = clamp_id(ids.b0), b1 = clamp_id(ids.b1);
+    // clamped here, at use, so the loads of the ids stay in flight until
+    // then; on the scalar unit, before the lane's choice between the two
+    int b0 = clamp_id(ids.b0), b1 = clamp_id(ids.b1);
+    asm("" : "+s"(b0), "+s"(b1));
     const uint32_t blk = (uint32_t)(lane_b1 ? b1 : b0);
     const int in_block = BS == 64 ? ((kq0 + step) * 32) % 64 : 0;
     return lane_base + (uint64_t)blk * bstride + in_block * key_bytes;
   };
-  // byte offsets of this wave's fragments from its source address (uniform)
-  int frag_offs[FW];
-#pragma unroll
-  for (int jj = 0; jj < FW; ++jj) {
-    const int f = wave * FW + jj, v = f - KF;
-    frag_offs[jj] = moves_k ? (f / KL) * 64 + (f % KL) * 4 * BS * 16
-                            : (KV == KV_BF16 ? v * 16 * BS * 2 : v * 32 * BS);
+  // This wave's fragments are consecutive granules of one K sub-tile, or
+  // consecutive V fragments: the first one's offset joins the lane's base,
+  // and the others follow at a fixed stride.
+  static_assert(KL % FW == 0, "a wave's K fragments lie in one sub-tile");
+  const int fstride = moves_k ? 4 * BS * 16 : (KV == KV_BF16 ? 16 * BS * 2 : 32 * BS);
+  {
+    const int f = wave * FW, v = f - KF;
+    lane_base += moves_k ? (f / KL) * 64 + (f % KL) * fstride : v * fstride;
   }
-  auto frag_off = [&](int jj) -> int { return frag_offs[jj]; };
   auto slot = [&](int st, int jj) -> char* { return ring + st * T::STAGE + (wave * FW + jj) * 1024; };
 
   // DMA this wave's share of step `step` into stage `st`
@@ -346,7 +348,7 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
     const char* src = step_src(step, ids);
 #pragma unroll
     for (int jj = 0; jj < FW; ++jj)
-      __builtin_amdgcn_global_load_lds((const void*)(src + frag_off(jj)),
+      __builtin_amdgcn_global_load_lds((const void*)(src + jj * fstride),
                                        (lds_void_t*)slot(st, jj), 16, 0, 0);
   };
   // ids of the next step to fetch, loaded one fetch ahead
