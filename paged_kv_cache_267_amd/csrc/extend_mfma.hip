@@ -160,6 +160,26 @@ __device__ __forceinline__ ExSeq seq_of_rank(const ExtendParams& p, int r, int l
           __builtin_amdgcn_readlane(mine.n, s)};
 }
 
+// DMA of fragments J, J+1, .. N-1 of a wave: the 16 bytes of lane l from src
+// + J * S to LDS dst0 + J * 1024 + 16 l.  The instruction's immediate offset
+// moves both the global and the LDS address, so it carries J * S and the LDS
+// base (M0) is set J * S below the fragment.  That base must stay at or above
+// dst0 (an LDS address below the workgroup's block drops the write), so only
+// strides up to a fragment's 1024 bytes go into the immediate; longer ones
+// are added to the global address.
+template <int S, int J, int N>
+__device__ __forceinline__ void dma_frags(const char* src, char* dst0) {
+  if constexpr (J < N) {
+    if constexpr (S <= 1024)
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(dst0 + J * (1024 - S)),
+                                       16, J * S, 0);
+    else
+      __builtin_amdgcn_global_load_lds((const void*)(src + J * S), (lds_void_t*)(dst0 + J * 1024),
+                                       16, 0, 0);
+    dma_frags<S, J + 1, N>(src, dst0);
+  }
+}
+
 template <int KV, int D, int BS, int NCB, int NBUF>
 struct ExtendTile {
   static constexpr int E = KvTraits<KV>::E;
@@ -260,7 +280,8 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
     accl[j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     m_ref[j] = EX_M_FLOOR;
   }
-  const bf16x8_t ones = as_bf16x8(BF16_ONE_X2, BF16_ONE_X2, BF16_ONE_X2, BF16_ONE_X2);
+  bf16x8_t ones = as_bf16x8(BF16_ONE_X2, BF16_ONE_X2, BF16_ONE_X2, BF16_ONE_X2);
+  asm("" : "+v"(ones));   // held in registers, not rebuilt in every step
   const float qk = p.qk_scale;
   // a raw score above thr[j] would put its weight above 2^EX_LAZY_LOG2 (qk > 0)
   float thr[NCB];
@@ -335,21 +356,20 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
   // consecutive V fragments: the first one's offset joins the lane's base,
   // and the others follow at a fixed stride.
   static_assert(KL % FW == 0, "a wave's K fragments lie in one sub-tile");
-  const int fstride = moves_k ? 4 * BS * 16 : (KV == KV_BF16 ? 16 * BS * 2 : 32 * BS);
+  constexpr int KSTR = 4 * BS * 16;                            // next K granule
+  constexpr int VSTR = KV == KV_BF16 ? 16 * BS * 2 : 32 * BS;  // next V fragment
   {
     const int f = wave * FW, v = f - KF;
-    lane_base += moves_k ? (f / KL) * 64 + (f % KL) * fstride : v * fstride;
+    lane_base += moves_k ? (f / KL) * 64 + (f % KL) * KSTR : v * VSTR;
   }
-  auto slot = [&](int st, int jj) -> char* { return ring + st * T::STAGE + (wave * FW + jj) * 1024; };
 
   // DMA this wave's share of step `step` into stage `st`
   auto fetch = [&](int step, int st, StepIds ids) {
     if (wave >= NFW) return;
     const char* src = step_src(step, ids);
-#pragma unroll
-    for (int jj = 0; jj < FW; ++jj)
-      __builtin_amdgcn_global_load_lds((const void*)(src + jj * fstride),
-                                       (lds_void_t*)slot(st, jj), 16, 0, 0);
+    char* dst0 = ring + st * T::STAGE + wave * FW * 1024;
+    if (moves_k) dma_frags<KSTR, 0, FW>(src, dst0);
+    else dma_frags<VSTR, 0, FW>(src, dst0);
   };
   // ids of the next step to fetch, loaded one fetch ahead
   StepIds next_ids = {0, 0};
