@@ -180,6 +180,19 @@ __device__ __forceinline__ void dma_frags(const char* src, char* dst0) {
   }
 }
 
+// Steps step0 + I, .., step0 + N - 1 (those below nsteps) of the walk, step
+// step0 + i in ring stage i.
+template <int I, int N, class F>
+__device__ __forceinline__ void ring_steps(F& f, int step0, int nsteps) {
+  if constexpr (I < N) {
+    if (step0 + I < nsteps) {
+      f(std::integral_constant<int, I>{}, std::integral_constant<int, (I + N - 1) % N>{},
+        step0 + I);
+      ring_steps<I + 1, N>(f, step0, nsteps);
+    }
+  }
+}
+
 template <int KV, int D, int BS, int NCB, int NBUF>
 struct ExtendTile {
   static constexpr int E = KvTraits<KV>::E;
@@ -389,12 +402,12 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
     next_ids = ids_of(min(step + NBUF, nsteps - 1));
   };
 
-  int cur_st = 0, ahead_st = NBUF - 1;   // stage of `step`, and of the step fetched in it
-  auto next_stages = [&]() {
-    cur_st = cur_st == NBUF - 1 ? 0 : cur_st + 1;
-    ahead_st = ahead_st == NBUF - 1 ? 0 : ahead_st + 1;
-  };
-  for (int step = 0; step < nsteps; ++step) {
+  // One step of the walk, in ring stage `stage_c` (an int, or a compile-time
+  // constant when the loop below is unrolled by the ring's depth: then the
+  // stage offsets of the LDS reads are immediates).
+  auto do_step = [&](auto stage_c, auto ahead_c, int step) {
+    const int cur_st = stage_c;     // stage of `step`
+    const int ahead_st = ahead_c;   // stage of the step fetched in it
     // this wave's share of `step` has landed; after the barrier everyone's
     // has, and every wave is done with the stage read one step earlier.  The
     // barrier orders LDS only: a full __syncthreads would also drain the
@@ -409,8 +422,7 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
     if (key0 + 32 <= klo || key0 >= khi) {  // no key of this wave's columns
       fetch_ahead(ahead, ahead_st);
       load_next_ids(step);
-      next_stages();
-      continue;
+      return;
     }
     const char* stage = ring + cur_st * T::STAGE;
 
@@ -567,7 +579,18 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
     }
     wave_priority<0>();
     load_next_ids(step);
-    next_stages();
+  };
+  if constexpr (KV == KV_FP8) {
+    // E4M3: unrolled (4 % faster on the E4M3 window workload; bf16 measured
+    // level on chunked prefill and 1.6 % slower on prefix extend)
+    for (int step0 = 0; step0 < nsteps; step0 += NBUF) ring_steps<0, NBUF>(do_step, step0, nsteps);
+  } else {
+    int st = 0, ast = NBUF - 1;
+    for (int step = 0; step < nsteps; ++step) {
+      do_step(st, ast, step);
+      st = st == NBUF - 1 ? 0 : st + 1;
+      ast = ast == NBUF - 1 ? 0 : ast + 1;
+    }
   }
   // no DMA may still be writing this workgroup's LDS when it ends
   wait_vmcnt<0>();
