@@ -31,6 +31,10 @@ __device__ __forceinline__ int folded_head(int r, int kk) {
   return 0;
 }
 
+// The reference max of a head is raised only when a score exceeds it by more
+// than 2^VALU_LAZY_LOG2 (base 2), so weights stay below 2^8.
+constexpr float VALU_LAZY_LOG2 = 8.0f;
+
 template <int KV_, int D_, int BS_, int G_>
 struct ValuTile {
   static constexpr int KV = KV_, D = D_, BS = BS_, G = G_;
@@ -172,20 +176,37 @@ struct ValuTile {
       sc[0] = swap_add16(f1[0], f1[0]);
     }
 
-    // mask and online softmax (base 2); every sub-tile holds a valid token
+    // mask and online softmax (base 2); every sub-tile holds a valid token.
+    // The reference max is raised lazily: only when a score exceeds it by
+    // more than 2^8 (one ballot over the wave) are the sub-tile's row maxima,
+    // the new references and the rescale factors formed; otherwise the
+    // weights are taken against the references as they stand, and the
+    // accumulators keep their scale.
     const int tok = st * 16 + col;
     const bool valid = tok >= t0 && tok < t1;
+    float xs[NGL];
+    bool over = false;
 #pragma unroll
     for (int kk = 0; kk < NGL; ++kk) {
-      const float x = valid ? sc[kk] * qk_scale : -INFINITY;
-      const float tmax = row_max16(x);
-      const float m_new = fmaxf(m_run[kk], tmax);
-      const float alpha = fast_exp2(m_run[kk] - m_new);
-      const float pv = fast_exp2(x - m_new);
-      l_run[kk] = l_run[kk] * alpha + pv;
-      m_run[kk] = m_new;
+      xs[kk] = valid ? sc[kk] * qk_scale : -INFINITY;
+      over |= xs[kk] > m_run[kk] + VALU_LAZY_LOG2;
+    }
+    const bool rescale = __builtin_amdgcn_ballot_w64(over) != 0;
+    if (rescale) {
+#pragma unroll
+      for (int kk = 0; kk < NGL; ++kk) {
+        const float m_new = fmaxf(m_run[kk], row_max16(xs[kk]));
+        const float alpha = fast_exp2(m_run[kk] - m_new);
+        l_run[kk] *= alpha;
+        m_run[kk] = m_new;
+        if (col == 0) wl.alpha[folded_head<G>(row, kk)] = alpha;
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < NGL; ++kk) {
+      const float pv = fast_exp2(xs[kk] - m_run[kk]);
+      l_run[kk] += pv;
       const int g = folded_head<G>(row, kk);
-      if (col == 0) wl.alpha[g] = alpha;
       if (KV == KV_F32) {
         wl.p[g][col] = __float_as_uint(pv);
       } else {
@@ -229,12 +250,14 @@ struct ValuTile {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // rescale and accumulate P.V
+    // rescale (when the references moved) and accumulate P.V
+    if (rescale) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float al = wl.alpha[g];
+      for (int g = 0; g < G; ++g) {
+        const float al = wl.alpha[g];
 #pragma unroll
-      for (int k = 0; k < VPL; ++k) acc[g][k] *= al;
+        for (int k = 0; k < VPL; ++k) acc[g][k] *= al;
+      }
     }
     if (KV == KV_F32) {
 #pragma unroll
