@@ -12,10 +12,11 @@
 //                     4 consecutive tokens of one V row per lane), B = P^T.
 // Heads sit on the N axis, so lane l owns head l%16 in every fragment: the S^T
 // C-fragment is bit for bit the P^T B-fragment, and a head's running max, sum
-// and rescale are lane-local.  Per sub-tile the only cross-lane step is the
-// column max over the 4 lane rows (two permlane swaps).  The running max is
-// updated lazily: accumulators are rescaled only when a head's max grows by
-// more than 2^8, so p <= 256.  E4M3 codes are converted to bf16 in registers
+// and rescale are lane-local.  The running max is updated lazily:
+// accumulators are rescaled only when a head's max grows by more than 2^8, so
+// p <= 256; a sub-tile finds that by comparing its scores with the reference
+// (one ballot), and only then forms the column max over the 4 lane rows (two
+// permlane swaps), the only cross-lane step.  E4M3 codes are converted to bf16 in registers
 // (exact; "vLLM 0.7.2 deep dive: PagedAttention v2 with FlashAttention-3",
 // jsqmd.com, s2.2); k_scale is folded into the score scale, v_scale applied at
 // the merge.
@@ -168,8 +169,12 @@ struct MfmaTile {
         for (int w = 0; w < VW; ++w) b.v[nb][w] &= vmask[w];
     }
 
-    const float cmax = colmax4(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-    if (__builtin_amdgcn_ballot_w64(cmax > m_ref + LAZY_RESCALE_LOG2) != 0) {
+    // only a score more than 2^8 above the reference calls for a rescale, so
+    // the column max is formed only when some lane holds one
+    const float thr = m_ref + LAZY_RESCALE_LOG2;
+    const bool over = sc[0] > thr || sc[1] > thr || sc[2] > thr || sc[3] > thr;
+    if (__builtin_amdgcn_ballot_w64(over) != 0) {
+      const float cmax = colmax4(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
       const float m_new = fmaxf(m_ref, cmax);
       const float alpha = fast_exp2(m_ref - m_new);
       l_run *= alpha;
