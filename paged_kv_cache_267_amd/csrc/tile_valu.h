@@ -12,11 +12,13 @@
 // come from one K read (bf16 v_dot2_f32_bf16, E4M3 converted to bf16 pairs
 // first, fp32 FMA for f32 caches).  Two cross-row swap-adds fold the 4 rows so
 // that each row ends with its own share of the G heads, fully summed
-// (transpose-reduce); a 16-lane DPP max gives the sub-tile max per head; the
-// running max / sum are base-2 (log2 e folded into the score scale).  p goes
-// to a per-wave LDS slot (bf16 pairs, fp32 for f32 caches) with the rescale
-// factors, and P.V accumulates with v_dot2_f32_bf16 (fp32 FMA) into per-lane
-// fp32 accumulators: lane l owns 16-byte pieces l, l+64, ... of the V sub-tile.
+// (transpose-reduce).  The softmax is base-2 (log2 e folded into the score
+// scale) against a per-head reference raised lazily: only when a score exceeds
+// it by more than 2^8 are the 16-lane DPP row maxima and the rescale factors
+// formed.  p goes to a per-wave LDS slot (bf16 pairs, fp32 for f32 caches),
+// with the rescale factors when there are any, and P.V accumulates with
+// v_dot2_f32_bf16 (fp32 FMA) into per-lane fp32 accumulators: lane l owns
+// 16-byte pieces l, l+64, ... of the V sub-tile.
 #pragma once
 
 #include "common.h"
