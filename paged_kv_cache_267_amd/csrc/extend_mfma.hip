@@ -16,11 +16,11 @@
 //
 // Work.  One workgroup of 4 waves takes one (sequence, KV head, column
 // block); each wave owns CW = 16 * NCB consecutive columns.  The workgroup
-// walks the keys its columns need, 32 per step, through a ring of NBUF LDS
+// walks the keys its columns need, 32 per step, through a ring of 4 LDS
 // stages: each wave moves a quarter of a step's K and V from the cache into
-// LDS with DMA loads (global_load_lds: no registers held while in flight),
-// NBUF - 1 steps ahead; one barrier per step publishes the stage and retires
-// the one read a step earlier.  Each wave then reads its MFMA operands from
+// LDS with DMA loads (global_load_lds: no registers held while in flight).
+// Steps go in pairs: one barrier publishes a pair's two stages and retires
+// the previous pair's, which then load the two steps after the pair.  Each wave then reads its MFMA operands from
 // LDS (one 16-byte read per lane and fragment, fragments laid out in lane
 // order, so the reads are conflict-free) and skips steps its own columns do
 // not need.  Column blocks of one (sequence, KV head) are dealt to one XCD
@@ -186,8 +186,7 @@ template <int I, int N, class F>
 __device__ __forceinline__ void ring_steps(F& f, int step0, int nsteps) {
   if constexpr (I < N) {
     if (step0 + I < nsteps) {
-      f(std::integral_constant<int, I>{}, std::integral_constant<int, (I + N - 1) % N>{},
-        step0 + I);
+      f(std::integral_constant<int, I>{}, std::integral_constant<bool, I % 2 == 0>{}, step0 + I);
       ring_steps<I + 1, N>(f, step0, nsteps);
     }
   }
@@ -384,44 +383,53 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
     if (moves_k) dma_frags<KSTR, 0, FW>(src, dst0);
     else dma_frags<VSTR, 0, FW>(src, dst0);
   };
-  // ids of the next step to fetch, loaded one fetch ahead
-  StepIds next_ids = {0, 0};
+  // Steps go in pairs over a ring of 4 stages: one wait and one barrier
+  // publish a pair's two steps, and after it the pair's refill loads the two
+  // steps after the next pair into the previous pair's stages (past the end
+  // the last step is fetched again: the count of loads in flight stays
+  // fixed).  Two steps are in flight while two are computed.
+  static_assert(NBUF == 4, "pairs of steps over a 4-stage ring");
+  // block ids of the next refill (steps p + 2, p + 3 for the pair at p)
+  StepIds next_a = {0, 0}, next_b = {0, 0};
   if (nsteps > 0) {
-#pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i) fetch(min(i, nsteps - 1), i, ids_of(min(i, nsteps - 1)));
-    next_ids = ids_of(min(NBUF - 1, nsteps - 1));
+    fetch(0, 0, ids_of(0));
+    fetch(min(1, nsteps - 1), 1, ids_of(min(1, nsteps - 1)));
+    next_a = ids_of(min(2, nsteps - 1));
+    next_b = ids_of(min(3, nsteps - 1));
   }
-  // fetch step `ahead` with the ids loaded in the step before
-  auto fetch_ahead = [&](int ahead, int st) { fetch(ahead, st, next_ids); };
-  // At the end of step `step`, once its LDS reads are consumed, load the ids
-  // the next step fetches: scalar loads share a counter with LDS reads, so
-  // issued earlier they would make the step's LDS waits wait for them too.
-  // The barrier at the top of the next step waits for them.
-  auto load_next_ids = [&](int step) {
+  auto refill = [&](int step, int st) {   // step: the pair's first, in stage st
+    fetch(min(step + 2, nsteps - 1), (st + 2) % NBUF, next_a);
+    fetch(min(step + 3, nsteps - 1), (st + 3) % NBUF, next_b);
+  };
+  // At the end of a pair's second step, once its LDS reads are consumed,
+  // load the ids of the next pair's refill: scalar loads share a counter
+  // with LDS reads, so issued earlier they would make the pair's LDS waits
+  // wait for them too.  The next pair's barrier waits for them.
+  auto load_next_ids = [&](int second) {
     asm volatile("" ::: "memory");
-    next_ids = ids_of(min(step + NBUF, nsteps - 1));
+    next_a = ids_of(min(second + 3, nsteps - 1));
+    next_b = ids_of(min(second + 4, nsteps - 1));
   };
 
   // One step of the walk, in ring stage `stage_c` (an int, or a compile-time
   // constant when the loop below is unrolled by the ring's depth: then the
-  // stage offsets of the LDS reads are immediates).
-  auto do_step = [&](auto stage_c, auto ahead_c, int step) {
+  // stage offsets of the LDS reads are immediates); `first_c` tells the
+  // pair's first step from its second.
+  auto do_step = [&](auto stage_c, auto first_c, int step) {
     const int cur_st = stage_c;     // stage of `step`
-    const int ahead_st = ahead_c;   // stage of the step fetched in it
-    // this wave's share of `step` has landed; after the barrier everyone's
-    // has, and every wave is done with the stage read one step earlier.  The
-    // barrier orders LDS only: a full __syncthreads would also drain the
-    // DMA loads of the later steps and serialise loading with computing.
-    wait_vmcnt<(NBUF - 2) * FW>();
-    ring_barrier();
-    // the stage to refill NBUF - 1 steps ahead (past the end the last step
-    // is fetched again: the count of loads in flight stays fixed)
-    const int ahead = min(step + NBUF - 1, nsteps - 1);
-
+    constexpr bool first = decltype(first_c)::value;
+    if (first) {
+      // this wave's share of the pair has landed; after the barrier
+      // everyone's has, and every wave is done with the previous pair's
+      // stages.  The barrier orders LDS only: a full __syncthreads would also
+      // drain the DMA loads of the later steps.
+      wait_vmcnt<0>();
+      ring_barrier();
+    }
     const int key0 = (kq0 + step) * 32;
     if (key0 + 32 <= klo || key0 >= khi) {  // no key of this wave's columns
-      fetch_ahead(ahead, ahead_st);
-      load_next_ids(step);
+      if (first) refill(step, cur_st);
+      else load_next_ids(step);
       return;
     }
     const char* stage = ring + cur_st * T::STAGE;
@@ -460,7 +468,7 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
     }
 
     // refill while the score products run
-    fetch_ahead(ahead, ahead_st);
+    if (first) refill(step, cur_st);
 
     // V operands: dword w holds keys 8r + 2w, 8r + 2w + 1 of dim 16nb + c
     uint32_t vq[NB][4];
@@ -578,18 +586,18 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
       }
     }
     wave_priority<0>();
-    load_next_ids(step);
+    if (!first) load_next_ids(step);
   };
   if constexpr (KV == KV_FP8) {
     // E4M3: unrolled (4 % faster on the E4M3 window workload; bf16 measured
     // level on chunked prefill and 1.6 % slower on prefix extend)
     for (int step0 = 0; step0 < nsteps; step0 += NBUF) ring_steps<0, NBUF>(do_step, step0, nsteps);
   } else {
-    int st = 0, ast = NBUF - 1;
-    for (int step = 0; step < nsteps; ++step) {
-      do_step(st, ast, step);
-      st = st == NBUF - 1 ? 0 : st + 1;
-      ast = ast == NBUF - 1 ? 0 : ast + 1;
+    int st = 0;   // stage of the pair's first step: 0 or 2
+    for (int step = 0; step < nsteps; step += 2) {
+      do_step(st, std::true_type{}, step);
+      if (step + 1 < nsteps) do_step(st + 1, std::false_type{}, step + 1);
+      st ^= 2;
     }
   }
   // no DMA may still be writing this workgroup's LDS when it ends
@@ -615,10 +623,10 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
   }
 }
 
-// Column blocks of 16 per wave, and LDS stages in the ring (NBUF - 1 steps
-// in flight while one is computed).
+// Column blocks of 16 per wave, and LDS stages in the ring (a pair of steps
+// in flight while a pair is computed).
 template <int D> constexpr int ex_ncb() { return D == 128 ? 2 : 4; }
-template <int D> constexpr int ex_nbuf() { return 3; }
+template <int D> constexpr int ex_nbuf() { return 4; }
 
 template <int KV, int D, int BS>
 hipError_t launch_ncb(const ExtendParams& p, hipStream_t stream) {
