@@ -411,10 +411,10 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
     next_b = ids_of(min(second + 4, nsteps - 1));
   };
 
-  // One step of the walk, in ring stage `stage_c` (an int, or a compile-time
-  // constant when the loop below is unrolled by the ring's depth: then the
-  // stage offsets of the LDS reads are immediates); `first_c` tells the
-  // pair's first step from its second.
+  // One step of the walk, in ring stage `stage_c` (a compile-time constant:
+  // the loop below is unrolled by the ring's depth, so the stage offsets of
+  // the LDS reads are immediates); `first_c` tells the pair's first step from
+  // its second.
   auto do_step = [&](auto stage_c, auto first_c, int step) {
     const int cur_st = stage_c;     // stage of `step`
     constexpr bool first = decltype(first_c)::value;
@@ -588,18 +588,8 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
     wave_priority<0>();
     if (!first) load_next_ids(step);
   };
-  if constexpr (KV == KV_FP8) {
-    // E4M3: unrolled (4 % faster on the E4M3 window workload; bf16 measured
-    // level on chunked prefill and 1.6 % slower on prefix extend)
-    for (int step0 = 0; step0 < nsteps; step0 += NBUF) ring_steps<0, NBUF>(do_step, step0, nsteps);
-  } else {
-    int st = 0;   // stage of the pair's first step: 0 or 2
-    for (int step = 0; step < nsteps; step += 2) {
-      do_step(st, std::true_type{}, step);
-      if (step + 1 < nsteps) do_step(st + 1, std::false_type{}, step + 1);
-      st ^= 2;
-    }
-  }
+  // unrolled by the ring's depth: each step's stage is a constant
+  for (int step0 = 0; step0 < nsteps; step0 += NBUF) ring_steps<0, NBUF>(do_step, step0, nsteps);
   // no DMA may still be writing this workgroup's LDS when it ends
   wait_vmcnt<0>();
 
