@@ -266,6 +266,21 @@ def test_extend_named_workload_parity(name):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("name", W.EXTEND_NAMES)
+def test_extend_repeat_runs_bit_identical(name):
+    """Each output column is computed by one wave in a fixed key order, so
+    every run gives the same bits (the LDS ring's reuse is race-free)."""
+    wl = W.extend_config(name)
+    _announce(f"extend repeat runs {name}")
+    dw = _gpu_extend(wl)
+    first = dw.out.clone()
+    for _ in range(6):
+        dw.extend()
+        torch.cuda.synchronize()
+        assert torch.equal(dw.out.view(torch.int16), first.view(torch.int16))
+
+
+@pytest.mark.gpu
 def test_extend_window_poison_variant():
     _announce("extend fp8 window with out-of-window blocks pointing at a NaN block")
     wl = W.extend_config("extend_fp8_window", poison_out_of_window=True)

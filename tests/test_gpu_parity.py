@@ -423,6 +423,48 @@ def test_config5_window_poison_variant():
 
 
 # ---------------------------------------------------------------------------
+# repeated runs: the cross-wave merges are race-free
+
+@pytest.mark.parametrize("kvdt", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("split", [False, True])
+def test_repeat_runs_bit_identical(kvdt, split):
+    """A segment's sub-tiles go round-robin to a half's 4 waves, whose states
+    are merged through LDS in wave order, and halves claim whole segments: so
+    every run must give the same bits.  A deposit read before it is complete,
+    or a merge area reused too early, would show as run-to-run differences.
+    Many segments per workgroup, long and short, so that batches, carried
+    segments and both merge areas are exercised; the first run is also
+    checked against the oracle."""
+    import torch
+    rng = np.random.default_rng(4242)
+    lens = rng.integers(1, 3000, size=96).tolist() + [1, 16, 17, 6000]
+    wl = W.random_case(4242, seq_lens=lens, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                       block_size=16, kv_dtype=kvdt, partition_size=256)
+    rows = np.sort(np.random.default_rng(7).choice(len(lens) * 32, 512, replace=False))
+    kc, vc = oracle_caches(wl)
+    ref = oracle_decode(wl, kc, vc, rows=rows)
+    for k in kernels(kvdt):
+        announce(f"repeat runs {kvdt} split={split} kernel={k}")
+        with pa.decode_kernel(k):
+            dw = gpu_run(wl, split=split)
+            first = dw.out.clone()
+            assert_close(dw.out_f64()[rows], ref, kvdt, f"repeat first run kernel={k}")
+            parts = (dw.part_out.clone(), dw.part_lse.clone()) if split else None
+            for _ in range(8):
+                if split:
+                    dw.decode_split()
+                    dw.reduce()
+                else:
+                    dw.decode_unsplit()
+                torch.cuda.synchronize()
+                assert torch.equal(dw.out.view(torch.int16), first.view(torch.int16))
+                if split:
+                    # bit patterns: partitions no run writes stay NaN
+                    assert torch.equal(dw.part_out.view(torch.int32), parts[0].view(torch.int32))
+                    assert torch.equal(dw.part_lse.view(torch.int32), parts[1].view(torch.int32))
+
+
+# ---------------------------------------------------------------------------
 # the step captured in a HIP graph
 
 @pytest.mark.parametrize("kvdt", ["bf16", "fp8_e4m3"])
