@@ -384,10 +384,10 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
     else dma_frags<VSTR, 0, FW>(src, dst0);
   };
   // Steps go in pairs over a ring of 4 stages: one wait and one barrier
-  // publish a pair's two steps, and after it the pair's refill loads the two
-  // steps after the next pair into the previous pair's stages (past the end
-  // the last step is fetched again: the count of loads in flight stays
-  // fixed).  Two steps are in flight while two are computed.
+  // publish a pair's two steps, and after it the pair's refill loads the
+  // next pair's two steps into the previous pair's stages (past the end the
+  // last step is fetched again: the count of loads in flight stays fixed).
+  // Two steps are in flight while two are computed.
   static_assert(NBUF == 4, "pairs of steps over a 4-stage ring");
   // block ids of the next refill (steps p + 2, p + 3 for the pair at p)
   StepIds next_a = {0, 0}, next_b = {0, 0};
