@@ -69,3 +69,29 @@ def half_ulp_bf16(x):
 def err_stats(got: np.ndarray, ref: np.ndarray):
     d = np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))
     return float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0
+
+
+def relocate_far(dw, min_bytes: int = (1 << 32) + (64 << 20)):
+    """Move a device workload's cache to the top of a pool large enough that
+    each cache spans more than min_bytes (default: past 4 GiB): block b goes to
+    block N - 1 - b, every other block holds the NaN poison, and the block
+    tables follow.  Relabelling the physical blocks leaves the attention
+    unchanged, so the oracle of the original layout still applies; what this
+    exercises is the kernels' address arithmetic beyond 32 bits."""
+    import torch
+    from paged_kv_cache_267_amd.workloads import POISON_BYTE
+    wl = dw.wl
+    elem = dw.key_cache.element_size()
+    per_block = wl.num_kv_heads * wl.head_dim * wl.block_size   # elements
+    n_big = max(wl.num_blocks, -(-min_bytes // (per_block * elem)) + 1)
+    old = torch.arange(wl.num_blocks, device=dw.key_cache.device)
+    new = n_big - 1 - old
+    for name in ("key_cache", "value_cache"):
+        small = getattr(dw, name)
+        big = torch.full((n_big * per_block * elem,), POISON_BYTE, dtype=torch.uint8,
+                         device=small.device).view(small.dtype).view(n_big, per_block)
+        big[new] = small.view(wl.num_blocks, per_block)[old]
+        setattr(dw, name, big.view(-1))
+    bt = dw.block_tables
+    dw.block_tables = torch.where(bt >= 0, n_big - 1 - bt, bt)
+    return n_big

@@ -266,6 +266,30 @@ def test_extend_named_workload_parity(name):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("kvdt", ["bf16", "fp8_e4m3"])
+def test_extend_blocks_past_4gib_of_cache(kvdt):
+    """Chunks over blocks at the top of a pool whose caches span more than
+    4 GiB (block b at N - 1 - b, NaN poison elsewhere), against the oracle of
+    the original layout."""
+    from paged_kv_cache_267_amd.harness import DeviceWorkload
+    from tests.helpers import relocate_far
+    wl = W.random_case(4444, seq_lens=[300, 2000, 129, 1500], q_lens=[300, 200, 17, 64],
+                       num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                       kv_dtype=kvdt, sliding_window=1000 if kvdt == "fp8_e4m3" else 0)
+    _announce(f"extend pool past 4 GiB {kvdt}")
+    kc, vc = oracle_caches(wl)
+    ref = oracle_extend(wl, kc, vc)
+    dw = DeviceWorkload(wl)
+    dw.fill_history()
+    dw.append_new()
+    relocate_far(dw)
+    assert dw.key_cache.numel() * dw.key_cache.element_size() > (1 << 32)
+    dw.extend()
+    torch.cuda.synchronize()
+    _assert_close(dw.out_f64(), ref, kvdt, f"extend pool past 4 GiB {kvdt}")
+
+
+@pytest.mark.gpu
 @pytest.mark.parametrize("name", W.EXTEND_NAMES)
 def test_extend_repeat_runs_bit_identical(name):
     """Each output column is computed by one wave in a fixed key order, so
