@@ -511,9 +511,9 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
     wave_priority<0>();
     // Softmax in two phases.  First, per column block: mask, running max
     // and the lazy rescale (a rare branch).  Then one branch-free run: the
-    // weights of block 0, then each block's P.V products interleaved with
-    // the next block's weights, so the exponentials of one column block
-    // issue while the matrix core works on the one before.
+    // weights of block 0, then each block's P.V products followed by the
+    // next block's weights; the other wave on the SIMD fills the gaps, its
+    // exponentials beside these products and the other way round.
     float scs[NCB][8];
 #pragma unroll
     for (int j = 0; j < NCB; ++j) {
@@ -558,11 +558,8 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
                             fast_exp2(__builtin_fmaf(scs[j][2 * i + 1], qk, -m_ref[j])));
       return as_bf16x8(pw[0], pw[1], pw[2], pw[3]);
     };
-    // Region j (fenced by scheduling barriers): block j's NB + 1 products,
-    // each followed by a share of block j+1's weight instructions.
     bf16x8_t pop = weights(0);
     wave_priority<1>();
-    if (KV == KV_BF16) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < NCB; ++j) {
       accl[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop, accl[j], 0, 0, 0);
@@ -570,20 +567,7 @@ __global__ __launch_bounds__(EX_WAVES * 64, EX_WG_PER_CU) void extend_kernel(con
       for (int nb = 0; nb < NB; ++nb)
         acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             as_bf16x8(vq[nb][0], vq[nb][1], vq[nb][2], vq[nb][3]), pop, acc[j][nb], 0, 0, 0);
-      if (j + 1 < NCB) {
-        const bf16x8_t next = weights(j + 1);
-        // E4M3 caches keep the compiler's order: their V conversions already
-        // fill the VALU there, and this order measured 5 % slower
-        if (KV == KV_BF16) {
-#pragma unroll
-          for (int i = 0; i < NB + 1; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        pop = next;
-      }
+      if (j + 1 < NCB) pop = weights(j + 1);
     }
     wave_priority<0>();
     if (!first) load_next_ids(step);
