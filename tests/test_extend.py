@@ -218,6 +218,60 @@ def test_extend_small_parity(kvdt, D, bs, G, window):
     _assert_close(dw.out_f64(), ref, kvdt, f"extend kv={kvdt} D={D} bs={bs} G={G} W={window}")
 
 
+def extend_sweep_cases(n, seed=4242):
+    """Seeded random extend shapes: cache dtype, G 1..16, head_dim, block size,
+    KV heads, 1-6 sequences whose cached part and chunk are drawn from edge
+    values (block and 32-key step boundaries) or at random, and a window that
+    is off, 1, random or wider than every sequence."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        kvdt = ["bf16", "fp8_e4m3"][i % 2]
+        G = [1, 2, 4, 8, 16][(i // 2) % 5]
+        D = int(rng.choice([64, 128]))
+        bs = int(rng.choice([16, 32, 64]))
+        Hkv = int(rng.integers(1, 4)) if G < 16 else int(rng.integers(1, 3))
+        S = int(rng.integers(1, 7))
+        edge_c = [0, 1, bs - 1, bs, bs + 1, 31, 32, 33, 2 * bs + 3]
+        edge_n = [1, 2, 15, 16, 17, 31, 32, 33, 64]
+        cached = [int(rng.choice(edge_c)) if rng.random() < 0.4 else int(rng.integers(0, 400))
+                  for _ in range(S)]
+        chunk = [int(rng.choice(edge_n)) if rng.random() < 0.4 else int(rng.integers(1, 121))
+                 for _ in range(S)]
+        window = {0: 0, 1: 1, 2: int(rng.integers(2, 300)), 3: 100000}[(i // 10) % 4]
+        cases.append(dict(i=i, kvdt=kvdt, G=G, D=D, bs=bs, Hkv=Hkv, window=window,
+                          lens=[c + q for c, q in zip(cached, chunk)], q_lens=chunk,
+                          seed=seed * 100 + i))
+    return cases
+
+
+def test_extend_sweep_cases_cover_the_grid():
+    cases = extend_sweep_cases(40)
+    assert {c["G"] for c in cases if c["window"] not in (0, 100000)} == {1, 2, 4, 8, 16}
+    assert {(c["kvdt"], c["D"]) for c in cases} == {(k, d) for k in ("bf16", "fp8_e4m3")
+                                                    for d in (64, 128)}
+    assert {c["bs"] for c in cases} == {16, 32, 64}
+    assert all(1 <= q <= L for c in cases for q, L in zip(c["q_lens"], c["lens"]))
+
+
+@pytest.mark.gpu
+def test_extend_random_shape_sweep():
+    """40 seeded cases against the oracle; the first failing case stops the
+    sweep and is named."""
+    for c in extend_sweep_cases(40):
+        what = (f"extend case {c['i']}: {c['kvdt']} D{c['D']} bs{c['bs']} G{c['G']} "
+                f"Hkv{c['Hkv']} lens {c['lens']} chunks {c['q_lens']} W{c['window']}")
+        _announce(what)
+        wl = W.random_case(c["seed"], seq_lens=c["lens"], q_lens=c["q_lens"],
+                           num_q_heads=c["G"] * c["Hkv"], num_kv_heads=c["Hkv"],
+                           head_dim=c["D"], block_size=c["bs"], kv_dtype=c["kvdt"],
+                           sliding_window=c["window"])
+        kc, vc = oracle_caches(wl)
+        ref = oracle_extend(wl, kc, vc)
+        dw = _gpu_extend(wl)
+        _assert_close(dw.out_f64(), ref, c["kvdt"], what)
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("nseq,kvdt,window", [(64, "bf16", 0), (65, "bf16", 0),
                                               (64, "fp8_e4m3", 90), (65, "fp8_e4m3", 90)])
