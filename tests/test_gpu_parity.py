@@ -113,6 +113,50 @@ def test_reshape_and_cache_both_mappings_bit_exact(kvdt, D, bs):
     assert np.array_equal(gv, vc.view(np.uint8))
 
 
+@pytest.mark.parametrize("kvdt", ["bf16", "fp8_e4m3", "f32"])
+def test_reshape_and_cache_chunks_and_lone_tokens_bit_exact(kvdt):
+    """One append of fewer than 4096 tokens (the element-per-thread mapping)
+    mixing chunk runs (consecutive slots, one crossing two block boundaries,
+    one filling a whole block), lone tokens in blocks of their own, a
+    descending run and -1 padding.  Tokens of a run and lone tokens take
+    different store paths; all land where the oracle puts them, bit for bit."""
+    import torch
+    import paged_kv_cache_267_amd as pa
+    announce(f"reshape_and_cache chunks and lone tokens {kvdt}")
+    H, D, bs, NB = 2, 128, 16, 64
+    rng = np.random.default_rng(31)
+    slots = list(range(3 * bs + 5, 3 * bs + 42))                 # blocks 3, 4 and 5
+    slots += [int(b) * bs + int(rng.integers(0, bs))
+              for b in rng.choice(np.arange(10, 40), size=20, replace=False)]
+    slots += [-1, -1]
+    slots += list(range(45 * bs + 12, 45 * bs + 2, -1))          # descending
+    slots += list(range(50 * bs, 51 * bs))                       # a whole block
+    slots += [-1]
+    slots += list(range(60 * bs + 3, 60 * bs + 9))
+    sl = np.array(slots, np.int32)
+    T = sl.shape[0]
+    valid = sl[sl >= 0]
+    assert len(set(valid.tolist())) == valid.shape[0], "one token per slot"
+    npdt = {"bf16": np.uint16, "fp8_e4m3": np.uint8, "f32": np.float32}[kvdt]
+    tdt = {"bf16": torch.bfloat16, "fp8_e4m3": torch.uint8, "f32": torch.float32}[kvdt]
+    E = np.dtype(npdt).itemsize
+    raw_k = rng.integers(0, 256, size=(T, H, D * E), dtype=np.uint8)
+    raw_v = rng.integers(0, 256, size=(T, H, D * E), dtype=np.uint8)
+    kc_o = np.full(NB * H * D * bs * E, 0xA5, np.uint8).view(npdt)
+    vc_o = kc_o.copy()
+    oracle.reshape_and_cache(raw_k.view(npdt).reshape(T, H, D), raw_v.view(npdt).reshape(T, H, D),
+                             kc_o, vc_o, sl, num_kv_heads=H, head_dim=D, block_size=bs,
+                             num_blocks=NB, kv_dtype=kvdt)
+    key = torch.from_numpy(raw_k).cuda().view(tdt).reshape(T, H, D)
+    val = torch.from_numpy(raw_v).cuda().view(tdt).reshape(T, H, D)
+    kc = torch.full((NB * H * D * bs * E,), 0xA5, dtype=torch.uint8).cuda().view(tdt)
+    vc = kc.clone()
+    pa.pa_reshape_and_cache(key, val, kc, vc, torch.from_numpy(sl).cuda(), block_size=bs)
+    torch.cuda.synchronize()
+    assert np.array_equal(kc.view(torch.uint8).cpu().numpy(), kc_o.view(np.uint8))
+    assert np.array_equal(vc.view(torch.uint8).cpu().numpy(), vc_o.view(np.uint8))
+
+
 def test_reshape_and_cache_skips_negative_and_out_of_pool_slots():
     import torch
     import paged_kv_cache_267_amd as pa
