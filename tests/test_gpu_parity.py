@@ -98,14 +98,15 @@ def test_reshape_and_cache_bit_exact(kvdt, D, bs):
 @pytest.mark.parametrize("kvdt,D,bs", [("bf16", 128, 16), ("fp8_e4m3", 64, 32),
                                        ("f32", 128, 64)])
 def test_reshape_and_cache_both_mappings_bit_exact(kvdt, D, bs):
-    """The history fill writes more than 4096 tokens (the token-per-lane
-    mapping) and the step's append a few (the element-per-thread mapping):
-    both land where the oracle puts them, in the same cache."""
+    """The history fill writes more than 640 KiB of V (the token-per-lane
+    mapping) and the step's append a few tokens (the element-per-thread
+    mapping): both land where the oracle puts them, in the same cache."""
     announce(f"reshape_and_cache, long history {kvdt} D{D} bs{bs}")
     qdt = "f32" if kvdt == "f32" else "bf16"
     wl = W.random_case(22, seq_lens=[1, 17, 100, 2600, 3000], num_q_heads=4, num_kv_heads=2,
                        head_dim=D, block_size=bs, q_dtype=qdt, kv_dtype=kvdt)
-    assert wl.hist_slots.shape[0] > 4096 and wl.new_slots.shape[0] <= 4096
+    vbytes = lambda n: n * wl.num_kv_heads * D * W.ELEM_BYTES[kvdt]
+    assert vbytes(wl.hist_slots.shape[0]) > 640 << 10 >= vbytes(wl.new_slots.shape[0])
     dw = gpu_run(wl, split=False)
     gk, gv = dw.cache_bytes()
     kc, vc = oracle_caches(wl)
@@ -115,7 +116,7 @@ def test_reshape_and_cache_both_mappings_bit_exact(kvdt, D, bs):
 
 @pytest.mark.parametrize("kvdt", ["bf16", "fp8_e4m3", "f32"])
 def test_reshape_and_cache_chunks_and_lone_tokens_bit_exact(kvdt):
-    """One append of fewer than 4096 tokens (the element-per-thread mapping)
+    """One append of less than 640 KiB of V (the element-per-thread mapping)
     mixing chunk runs (consecutive slots, one crossing two block boundaries,
     one filling a whole block), lone tokens in blocks of their own, a
     descending run and -1 padding.  Tokens of a run and lone tokens take
