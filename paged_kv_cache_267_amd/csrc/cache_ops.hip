@@ -96,8 +96,9 @@ __global__ __launch_bounds__(256) void reshape_and_cache_rows_kernel(
   // their lines together: those stores stay in L2, which merges them (stored
   // non-temporal, each would reach memory on its own: a prefix-extend append
   // took 71 us instead of 21).
-  const bool chained = (tp != t && o > 0 && prev == slot - 1) ||
-                       (tn != t && o + 1 < bs && next == slot + 1);
+  // (unsigned: slot + 1 may exceed INT_MAX in a pool of more than 2^31 slots)
+  const bool chained = (tp != t && o > 0 && (unsigned)prev + 1u == (unsigned)slot) ||
+                       (tn != t && o + 1 < bs && (unsigned)slot + 1u == (unsigned)next);
   if (!chained) {
     if (E == 4) __builtin_nontemporal_store(v, (uint32_t*)dst);
     else if (E == 2) __builtin_nontemporal_store((uint16_t)v, (uint16_t*)dst);
