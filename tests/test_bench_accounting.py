@@ -65,7 +65,7 @@ def test_decode_bytes_equal_enumeration(case, partition_size):
 
 
 def test_decode_bytes_named_config_closed_form():
-    # config 1 holds no window and no split: 2 L D e per (sequence, KV head),
+    # the tiny f32 workload (4 sequences) holds no window and no split: 2 L D e per (sequence, KV head),
     # ceil(L / bs) table entries, one query and one output row per query head
     wl = W.config(1)
     e, eq, D = W.ELEM_BYTES[wl.kv_dtype], W.ELEM_BYTES[wl.q_dtype], wl.head_dim

@@ -455,8 +455,8 @@ def test_named_config_parity(cfg):
                 assert np.array_equal(gk, kc.view(np.uint8)) and np.array_equal(gv, vc.view(np.uint8))
 
 
-def test_config5_window_poison_variant():
-    announce("config 5 with out-of-window blocks pointing at a NaN block")
+def test_fp8_window_workload_poison_variant():
+    announce("E4M3 4K-window workload (256 sequences) with out-of-window blocks pointing at a NaN block")
     wl = W.config(5, poison_out_of_window=True)
     rows = _rows_sample(wl, 2048, seed=1)
     kc, vc = oracle_caches(wl)

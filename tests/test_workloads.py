@@ -67,7 +67,7 @@ def test_generator_is_deterministic():
     assert a.k_scale == b.k_scale
 
 
-def test_config1_shape_and_bytes():
+def test_tiny_f32_workload_shape_and_bytes():
     wl = W.config(1)
     assert list(wl.seq_lens) == [1, 17, 33, 100]
     assert wl.num_blocks == 64
