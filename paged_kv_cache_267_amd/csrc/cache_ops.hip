@@ -194,6 +194,75 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
     vc[tile + ((size_t)grp * 16 + e) * bs + o] = (uint8_t)e4m3_from_f32(xv[e] / v_scale);
 }
 
+// The same quantise-on-write for small appends (a decode step: one token per
+// sequence, each in a block of its own), one thread per (token, head,
+// element d), d fastest, as reshape_and_cache_rows_kernel: the 64 lanes of a
+// V store write 64 rows of one token; threads d < D / 16 also quantise and
+// write K group d.  The codes are those of reshape_and_cache_fp8_kernel (the
+// same quotient and rounding).  A token alone in its block of the launch is
+// stored non-temporal, as in the bit copy.  A launch covers tokens t_base ..
+// t_base + nt - 1 (nt * D <= 2^30) and heads h_base + blockIdx.y.
+template <int SE>
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_rows_kernel(
+    const uint8_t* __restrict__ key, const uint8_t* __restrict__ value,
+    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, const int32_t* __restrict__ slots,
+    int nt, int t_base, int h_base, int Hkv, int D, int bs, long long num_slots, float k_scale,
+    float v_scale) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i >= nt * D) return;
+  const int t = t_base + (int)((unsigned)i / (unsigned)D), d = (int)((unsigned)i % (unsigned)D);
+  const int h = h_base + (int)blockIdx.y;
+  const size_t row = ((size_t)t * Hkv + h) * D * SE;
+  const bool kgroup = d < D / 16;
+  const int slot = slots[t];
+  const int tp = max(t - 1, t_base), tn = min(t + 1, t_base + nt - 1);
+  const int prev = slots[tp], next = slots[tn];
+  const uint32_t vraw = SE == 4 ? *(const uint32_t*)(value + row + 4 * d)
+                                : (uint32_t)*(const uint16_t*)(value + row + 2 * d);
+  u32x4_t kr[SE];   // K group d: 16 source elements, 16 bytes at a time
+#pragma unroll
+  for (int c = 0; c < SE; ++c)
+    kr[c] = kgroup ? *(const u32x4_t*)(key + row + (size_t)d * 16 * SE + 16 * c)
+                   : (u32x4_t){0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int c = 0; c < SE; ++c) asm volatile("" ::"v"(kr[c]), "v"(vraw));  // loads ahead of the test
+  if (slot < 0 || (long long)slot >= num_slots) return;
+  const int b = slot / bs, o = slot % bs;
+  const size_t tile = ((size_t)b * Hkv + h) * (size_t)D * bs;
+  const float xv = SE == 4 ? __uint_as_float(vraw) : __uint_as_float(vraw << 16);
+  const uint8_t vq = (uint8_t)e4m3_from_f32(xv / v_scale);
+  uint32_t kq[4] = {0u, 0u, 0u, 0u};
+  if (kgroup) {
+#pragma unroll
+    for (int c = 0; c < SE; ++c) {
+      const uint32_t kw[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if (SE == 4) {
+          const int e = 4 * c + w;
+          kq[e >> 2] |= e4m3_from_f32(__uint_as_float(kw[w]) / k_scale) << (8 * (e & 3));
+        } else {
+          const int e = 8 * c + 2 * w;
+          kq[e >> 2] |= e4m3_from_f32(bf16_lo(kw[w]) / k_scale) << (8 * (e & 3));
+          kq[(e + 1) >> 2] |= e4m3_from_f32(bf16_hi(kw[w]) / k_scale) << (8 * ((e + 1) & 3));
+        }
+      }
+    }
+  }
+  uint8_t* vdst = vc + tile + (size_t)d * bs + o;
+  uint8_t* kdst = kc + tile + ((size_t)d * bs + o) * 16;
+  const bool chained = (tp != t && o > 0 && (unsigned)prev + 1u == (unsigned)slot) ||
+                       (tn != t && o + 1 < bs && (unsigned)slot + 1u == (unsigned)next);
+  if (!chained) {
+    __builtin_nontemporal_store(vq, vdst);
+    if (kgroup) __builtin_nontemporal_store((u32x4_t){kq[0], kq[1], kq[2], kq[3]}, (u32x4_t*)kdst);
+    asm volatile("" ::: "memory");   // not merged with the plain stores below
+  } else {
+    *vdst = vq;
+    if (kgroup) *(u32x4_t*)kdst = (u32x4_t){kq[0], kq[1], kq[2], kq[3]};
+  }
+}
+
 // Merge of per-partition results by their log-sum-exp: for each (sequence,
 // query head) with keys [lo, L), the partitions p with [pP, (p+1)P) meeting that
 // range are combined as sum_p e^(lse_p - M) o_p / sum_p e^(lse_p - M).
@@ -417,6 +486,17 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void
   const long long nslots = (long long)num_blocks * bs;
   const uint8_t *k8 = (const uint8_t*)key, *v8 = (const uint8_t*)value;
   uint8_t *kc8 = (uint8_t*)kc, *vc8 = (uint8_t*)vc;
+  // the bit copy's rule: appends of at most RC_ROWS_MAX_BYTES of V take the
+  // element-per-thread mapping
+  if ((long long)T * Hkv * D <= RC_ROWS_MAX_BYTES)
+    return for_each_chunk(T, Hkv, D, [&](dim3 grid, int nt, int t0, int h0) {
+      if (src_bytes == 4)
+        hipLaunchKernelGGL(reshape_and_cache_fp8_rows_kernel<4>, grid, dim3(256), 0, stream, k8,
+                           v8, kc8, vc8, slots, nt, t0, h0, Hkv, D, bs, nslots, k_scale, v_scale);
+      else
+        hipLaunchKernelGGL(reshape_and_cache_fp8_rows_kernel<2>, grid, dim3(256), 0, stream, k8,
+                           v8, kc8, vc8, slots, nt, t0, h0, Hkv, D, bs, nslots, k_scale, v_scale);
+    });
   return for_each_chunk(T, Hkv, D / 16, [&](dim3 grid, int nt, int t0, int h0) {
     if (src_bytes == 4)
       hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<4>, grid, dim3(256), 0, stream, k8, v8,

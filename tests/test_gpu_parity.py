@@ -186,6 +186,46 @@ def test_reshape_and_cache_skips_negative_and_out_of_pool_slots():
 
 
 @pytest.mark.parametrize("src", ["bf16", "f32"])
+def test_reshape_and_cache_fp8_large_append_bit_exact(src):
+    """Quantise-on-write of an append above 640 KiB of codes (the
+    token-per-lane mapping; the tests below stay under it): chunk runs and
+    scattered tokens, whole caches bit for bit against the oracle."""
+    import torch
+    import paged_kv_cache_267_amd as pa
+    announce(f"quantise-on-write, large append {src}")
+    H, D, bs, NB = 2, 128, 16, 1300   # 120 blocks of runs, one block per lone token
+    rng = np.random.default_rng(62)
+    T = 3000
+    assert T * H * D > 640 << 10
+    perm = rng.permutation(NB)
+    runs = np.concatenate([perm[b] * bs + np.arange(bs) for b in range(120)])   # 1920 in runs
+    lone = perm[120:120 + T - runs.size] * bs + rng.integers(0, bs, T - runs.size)
+    slots = np.concatenate([runs, lone]).astype(np.int32)
+    x = (rng.standard_normal((2, T, H, D)) * np.exp(rng.uniform(-8, 5, (2, T, H, D)))).astype(
+        np.float32)
+    if src == "bf16":
+        k_in = (x[0].view(np.uint32) >> 16).astype(np.uint16)
+        v_in = (x[1].view(np.uint32) >> 16).astype(np.uint16)
+        k_dev = torch.from_numpy(k_in.view(np.int16)).cuda().view(torch.bfloat16)
+        v_dev = torch.from_numpy(v_in.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        k_in, v_in = x[0], x[1]
+        k_dev, v_dev = torch.from_numpy(k_in).cuda(), torch.from_numpy(v_in).cuda()
+    sk, sv = 0.0371, 3.7
+    kc_o = np.full(NB * H * D * bs, 0x5A, np.uint8)
+    vc_o = kc_o.copy()
+    oracle.reshape_and_cache_fp8(k_in, v_in, kc_o, vc_o, slots, src_dtype=src, num_kv_heads=H,
+                                 head_dim=D, block_size=bs, num_blocks=NB, k_scale=sk, v_scale=sv)
+    kc = torch.full((NB * H * D * bs,), 0x5A, dtype=torch.uint8, device="cuda")
+    vc = kc.clone()
+    pa.pa_reshape_and_cache_fp8(k_dev, v_dev, kc, vc, torch.from_numpy(slots).cuda(),
+                                block_size=bs, k_scale=sk, v_scale=sv)
+    torch.cuda.synchronize()
+    assert np.array_equal(kc.cpu().numpy(), kc_o)
+    assert np.array_equal(vc.cpu().numpy(), vc_o)
+
+
+@pytest.mark.parametrize("src", ["bf16", "f32"])
 def test_reshape_and_cache_fp8_bit_exact(src):
     """Quantise-on-write against the oracle, whole caches bit for bit: every
     bf16 bit pattern (NaN, infinities, subnormals included) at three scales;
