@@ -88,8 +88,9 @@ __global__ __launch_bounds__(256) void reshape_and_cache_rows_kernel(
   const size_t tile = ((size_t)b * Hkv + h) * (size_t)D * bs * E;
   uint8_t* dst = vc + tile + ((size_t)d * bs + o) * E;
   uint8_t* kdst = kc + tile + ((size_t)d * bs + o) * 16;
-  // A token whose neighbours in the launch land in other blocks (a decode
-  // step's append: one token per sequence) leaves partial lines that nothing
+  // A token whose neighbours in the launch do not take the slots next to its
+  // own in its block (a decode step's append: one token per sequence) leaves
+  // partial lines that nothing
   // in the launch completes.  Stored non-temporal, they are not held dirty in
   // L2 for the write-back at the kernel's end, which the decode launched next
   // waits for (a decode step over 256 sequences of an E4M3 cache -3 %, over
