@@ -90,14 +90,13 @@ __global__ __launch_bounds__(256) void reshape_and_cache_rows_kernel(
   uint8_t* kdst = kc + tile + ((size_t)d * bs + o) * 16;
   // A token whose neighbours in the launch do not take the slots next to its
   // own in its block (a decode step's append: one token per sequence) leaves
-  // partial lines that nothing
-  // in the launch completes.  Stored non-temporal, they are not held dirty in
-  // L2 for the write-back at the kernel's end, which the decode launched next
-  // waits for (a decode step over 256 sequences of an E4M3 cache -3 %, over
-  // 64 sequences of a bf16 cache -1.6 %).  A chunk's tokens fill
-  // their lines together: those stores stay in L2, which merges them (stored
-  // non-temporal, each would reach memory on its own: a prefix-extend append
-  // took 71 us instead of 21).
+  // partial lines that nothing in the launch completes.  Stored non-temporal,
+  // they are not held dirty in L2 for the write-back at the kernel's end,
+  // which the decode launched next waits for (a decode step over 256
+  // sequences of an E4M3 cache -3 %, over 64 sequences of a bf16 cache
+  // -1.6 %).  A chunk's tokens fill their lines together: those stores stay
+  // in L2, which merges them (stored non-temporal, each would reach memory on
+  // its own: a prefix-extend append took 71 us instead of 21).
   // (unsigned: slot + 1 may exceed INT_MAX in a pool of more than 2^31 slots)
   const bool chained = (tp != t && o > 0 && (unsigned)prev + 1u == (unsigned)slot) ||
                        (tn != t && o + 1 < bs && (unsigned)slot + 1u == (unsigned)next);
